@@ -1,0 +1,314 @@
+"""Benchmark: row-wise norm forward + backward on one MI355X.
+
+One step = the whole path on one batch: forward (stats, normalise, affine) and
+backward (dx, per-workgroup dW/dB partials, column sum).  Default workload: LayerNorm
+2048 x 4096 bf16 with trainable weight and bias.  Prints ONE JSON line.
+
+Timing.  Inputs are resident in HBM before the timed region.  S independent buffer
+sets (> 2x the 256 MiB MALL in total) rotate through the steps, and step k runs the
+forward on set k and the backward on set k + S/2, so every kernel reads data that the
+preceding steps have evicted from L2 and MALL: the numbers are HBM numbers.  The K
+timed steps are replayed from a HIP graph (captured once; the library's calls never
+allocate or synchronise), bracketed by synchronisation; ms_per_step = wall / K.  The
+dominant kernel (backward stage 1) is then timed live with HIP events on the launch
+stream over an eager pass of the same steps: an event before the backward call and
+the library's stage event between its two kernels.
+
+Algorithmic bytes (what the method must move, once each): forward reads x (and
+residual), w (and b) and writes y (and residual_out) and the fp32 row statistics;
+backward reads dy, x (or residual_out), dres_out, w and writes dx and fp32 dW/dB.
+The backward recomputes the statistics from x, so it reads none.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2**20
+
+
+def alg_bytes(wl: workloads.Workload, trainable: bool) -> dict:
+    bx = 2 if wl.io in ("bf16", "fp16") else 4
+    bw = 2 if wl.wt in ("bf16", "fp16") else 4
+    M, N = wl.M, wl.N
+    mn = M * N * bx
+    if wl.op == "layernorm":
+        fwd = 2 * mn + N * bw * (2 if wl.bias else 1) + M * 8
+        bwd1 = 3 * mn + N * bw
+        grads = N * 4 * 2 if trainable else 0
+    elif wl.op == "rmsnorm":
+        fwd = 2 * mn + N * bw + M * 4
+        bwd1 = 3 * mn + N * bw
+        grads = N * 4 if trainable else 0
+    else:
+        fwd = 4 * mn + N * bw + M * 4
+        bwd1 = (4 if wl.dres else 3) * mn + N * bw
+        grads = N * 4 if trainable else 0
+    return {"fwd": fwd, "bwd_stage1": bwd1, "bwd": bwd1 + grads, "step": fwd + bwd1 + grads}
+
+
+class Sets:
+    """S resident copies of one workload's inputs and outputs."""
+
+    def __init__(self, wl, S, trainable, rn, torch):
+        self.wl, self.S, self.rn, self.torch = wl, S, rn, torch
+        base = workloads.generate(wl)
+        dev = torch.device("cuda:0")
+        self.eps, self.off = base["eps"], base["offset"]
+        M, N = wl.M, wl.N
+        self.sets = []
+        for s in range(S):
+            d = {}
+            for k in ("x", "residual", "dy", "dres"):
+                if k in base:
+                    d[k] = base[k].to(dev) if s == 0 else self.sets[0][k].clone()
+            d["w"] = base["w"].to(dev)
+            if "b" in base:
+                d["b"] = base["b"].to(dev)
+            d["y"] = torch.empty_like(d["x"])
+            d["dx"] = torch.empty_like(d["x"])
+            d["rstd"] = torch.empty(M, dtype=torch.float32, device=dev)
+            if wl.op == "layernorm":
+                d["mean"] = torch.empty(M, dtype=torch.float32, device=dev)
+            if wl.op == "fused_add_rmsnorm":
+                d["ro"] = torch.empty_like(d["x"])
+            ngr = (2 if wl.op == "layernorm" else 1) if trainable else 0
+            d["dw"] = torch.empty(N, dtype=torch.float32, device=dev) if trainable else None
+            d["db"] = (torch.empty(N, dtype=torch.float32, device=dev)
+                       if trainable and wl.op == "layernorm" else None)
+            need = rn.workspace_bytes(M, N, ngr) if ngr else 0
+            d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+            self.sets.append(d)
+        self.bytes_per_set = sum(v.numel() * v.element_size() for v in self.sets[0].values()
+                                 if isinstance(v, torch.Tensor))
+
+    def fwd(self, s):
+        d, rn, wl = self.sets[s], self.rn, self.wl
+        if wl.op == "rmsnorm":
+            rn.rmsnorm_fwd(d["x"], d["w"], self.eps, self.off, y=d["y"], rstd=d["rstd"])
+        elif wl.op == "layernorm":
+            rn.layernorm_fwd(d["x"], d["w"], d.get("b"), self.eps, y=d["y"], mean=d["mean"],
+                             rstd=d["rstd"])
+        else:
+            rn.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["w"], self.eps, self.off, y=d["y"],
+                                     residual_out=d["ro"], rstd=d["rstd"])
+
+    def bwd(self, s):
+        d, rn, wl = self.sets[s], self.rn, self.wl
+        if wl.op == "rmsnorm":
+            rn.rmsnorm_bwd(d["dy"], d["x"], d["w"], self.eps, self.off, dx=d["dx"], dw=d["dw"],
+                           workspace=d["ws"])
+        elif wl.op == "layernorm":
+            rn.layernorm_bwd(d["dy"], d["x"], d["w"], self.eps, dx=d["dx"], dw=d["dw"], db=d["db"],
+                             workspace=d["ws"])
+        else:
+            rn.fused_add_rmsnorm_bwd(d["dy"], d["ro"], d["w"], self.eps, self.off, d.get("dres"),
+                                     dx=d["dx"], dw=d["dw"], workspace=d["ws"])
+
+    def step(self, k):
+        self.fwd(k % self.S)
+        self.bwd((k + self.S // 2) % self.S)
+
+
+def n_sets(bytes_per_set: int) -> int:
+    s = 2
+    while s * bytes_per_set < 3 * MALL_BYTES:
+        s += 2
+    return max(s, 4)
+
+
+def time_steps(sets, K, W, use_graph, torch):
+    """Wall-clock seconds for K steps (after W warmup steps)."""
+    stream = torch.cuda.current_stream()
+    for k in range(W):
+        sets.step(k)
+    torch.cuda.synchronize()
+    if use_graph:
+        G = min(K, max(sets.S, 64))
+        G -= G % sets.S
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for k in range(G):
+                    sets.step(k)
+        torch.cuda.synchronize()
+        reps = max(1, K // G)
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, reps * G
+    t0 = time.perf_counter()
+    for k in range(K):
+        sets.step(k)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, K
+
+
+def event_times(sets, n, rn, torch):
+    """Per-kernel device time (us) from HIP events on the launch stream: forward,
+    backward stage 1 (dx + partials) and the whole backward call."""
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    trainable = sets.sets[0]["dw"] is not None or sets.sets[0]["db"] is not None
+    for k in range(n):
+        e0, e1, e2, e3 = ev[k]
+        e0.record(st)
+        sets.fwd(k % sets.S)
+        e1.record(st)
+        if trainable:
+            e2.record(st)       # materialise the handle, then let the library re-record it
+            rn.set_stage_event(e2)
+        sets.bwd((k + sets.S // 2) % sets.S)
+        if trainable:
+            rn.set_stage_event(None)
+        else:
+            e2.record(st)
+        e3.record(st)
+    torch.cuda.synchronize()
+    f = [ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(n)]
+    b1 = [ev[k][1].elapsed_time(ev[k][2]) * 1e3 for k in range(n)]
+    b = [ev[k][1].elapsed_time(ev[k][3]) * 1e3 for k in range(n)]
+    med = lambda a: sorted(a)[len(a) // 2]
+    mean = lambda a: sum(a) / len(a)
+    return {"fwd_us_median": med(f), "bwd_stage1_us_median": med(b1), "bwd_us_median": med(b),
+            "bwd_stage1_us_mean": mean(b1), "fwd_us_mean": mean(f)}
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The oracle (numpy fp64, as it stands) on a bounded sample of the workload's rows,
+    forward + backward, repeated until `budget_s` of CPU time has passed."""
+    import numpy as np
+    import oracle
+    rows = min(wl.M, 256)
+    t = workloads.generate(wl, rows=slice(0, rows))
+    f = workloads.as_f64
+    x, dy, w = f(t["x"]), f(t["dy"]), f(t["w"])
+    eps, off = t["eps"], t["offset"]
+    sub = workloads.Workload(wl.name, wl.op, rows, wl.N, wl.io, wl.wt, wl.eps, wl.offset,
+                             wl.weight, wl.bias, wl.dres)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        if wl.op == "rmsnorm":
+            oracle.rmsnorm_fwd(x, w, eps, off)
+            oracle.rmsnorm_bwd(dy, x, w, eps, off)
+        elif wl.op == "layernorm":
+            b = f(t["b"]) if "b" in t else None
+            oracle.layernorm_fwd(x, w, b, eps)
+            oracle.layernorm_bwd(dy, x, w, eps)
+        else:
+            r = f(t["residual"])
+            _, s_q, _ = oracle.fused_add_rmsnorm_fwd(x, r, w, eps, off, wl.io)
+            oracle.fused_add_rmsnorm_bwd(dy, f(t["dres"]) if "dres" in t else None, s_q, w, eps, off)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / n
+    gbs = alg_bytes(sub, True)["step"] / per / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {wl.M} rows x {wl.N}, fwd+bwd, {n} repetitions in {el:.1f} s "
+                      f"(numpy fp64, single thread)",
+            "us_per_step_of_sample": round(per * 1e6, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default=workloads.LAYERNORM_2048x4096.name,
+                    choices=sorted(workloads.BY_NAME))
+    ap.add_argument("--frozen", action="store_true", help="time the frozen-parameter step")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--event-steps", type=int, default=200)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no communication except one dW/dB all-reduce; "
+              "see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import normalization_row_wise_amd as rn
+
+    wl = workloads.BY_NAME[args.config]
+    trainable = not args.frozen
+    probe = Sets(wl, 1, trainable, rn, torch)
+    S = n_sets(probe.bytes_per_set)
+    del probe
+    sets = Sets(wl, S, trainable, rn, torch)
+
+    secs, k = time_steps(sets, args.steps, args.warmup, not args.eager, torch)
+    ab = alg_bytes(wl, trainable)
+    ms = secs / k * 1e3
+    gbs = ab["step"] * k / secs / 1e9
+    ev = event_times(sets, args.event_steps, rn, torch)
+
+    # frozen-parameter variant of the same step (context for the pruning)
+    other = {}
+    if trainable:
+        fz = Sets(wl, S, False, rn, torch)
+        fsecs, fk = time_steps(fz, args.steps, args.warmup, not args.eager, torch)
+        fev = event_times(fz, args.event_steps, rn, torch)
+        other = {"frozen_us_per_step": round(fsecs / fk * 1e6, 3),
+                 "frozen_bwd_us_median": round(fev["bwd_us_median"], 3)}
+        del fz
+
+    stage1_us = ev["bwd_stage1_us_mean"] if trainable else ev["bwd_us_median"]
+    achieved = ab["bwd_stage1"] / (stage1_us * 1e-6) / 1e9
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) & µs/call, bf16 norm fwd+bwd at M×N",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": k,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{wl.io} io, fp64 row statistics",
+        "data": "synthetic (seeded CPU randn, no dataset)",
+        "config": {"workload": wl.name, "op": wl.op, "M": wl.M, "N": wl.N, "io": wl.io,
+                   "weight": wl.wt, "trainable_params": trainable,
+                   "timing": "eager" if args.eager else "hip graph replay", "buffer_sets": S},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_call": {"fwd": round(ev["fwd_us_median"], 3),
+                        "bwd_stage1": round(ev["bwd_stage1_us_median"], 3),
+                        "bwd": round(ev["bwd_us_median"], 3),
+                        "fwd_plus_bwd": round(ev["fwd_us_median"] + ev["bwd_us_median"], 3)},
+        **other,
+        "roofline": {"kernel": "bwd_kernel (stage 1: dx + dW/dB partial rows)" if trainable
+                     else "bwd_kernel (frozen)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": ab["bwd_stage1"],
+                     "avg_launch_us": round(stage1_us, 3)},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * rownorm.h — C ABI of the row-wise normalisation library for AMD MI355X (gfx950).
+ *
+ * Operations (forward and backward): RMSNorm, LayerNorm and FusedAddRMSNorm over the
+ * rows of an [M, N] matrix.  Sources, cited by page title and section:
+ *   [frozen] "perf(norm): skip dW/dB calculation when parameters are frozen (#1067)"
+ *            — Motivation, Key Changes: backward kernels whose weight/bias gradient
+ *            work is pruned at compile time when the parameter is frozen; unused
+ *            gradient pointers are passed as null.
+ *   [gemma]  "fix(cutedsl): fuse Gemma RMSNorm weight offset in FP32"
+ *            — Summary: the weight and the Gemma offset are passed separately and
+ *            added in (at least) FP32 inside the forward and backward kernels;
+ *            Testing Done: mixed FP32 weights, strided inputs, in-place backward,
+ *            residual-output gradients, hidden sizes up to 18432.
+ *
+ * Definitions (the pages name the operations but print no formulas; these are the
+ * textbook / torch.nn.functional conventions):
+ *   RMSNorm    y = x * rstd * (w + offset),  rstd = 1 / sqrt(mean_j x_j^2 + eps)
+ *   LayerNorm  y = (x - mean) * rstd * w + b, rstd = 1 / sqrt(var + eps), var biased
+ *   FusedAdd   residual_out = round(x + residual); y = RMSNorm(residual_out)
+ *   Backward   g = dy * weight_eff, xhat = normalised row
+ *     RMSNorm    dx = rstd * (g - xhat * mean_j(g * xhat))
+ *     LayerNorm  dx = rstd * (g - mean_j(g) - xhat * mean_j(g * xhat))
+ *     FusedAdd   dx = dres_out + RMSNorm backward at residual_out; dx is the gradient
+ *                of both x and residual
+ *     dw = sum over rows of dy * xhat, db = sum over rows of dy (fp32 outputs)
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major [M, N]; ld* is the row stride in ELEMENTS (ld >= N, the
+ *     last dimension is contiguous).  M >= 0, 1 <= N <= RN_MAX_N.
+ *   - x, residual, y, residual_out, dy, dres_out and dx share the I/O type `xt`;
+ *     w and b share the weight type `wt`, which is `xt` or RN_F32 (mixed precision).
+ *     rstd, mean, dw and db are float32.
+ *   - All pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises: every call only enqueues kernels on `stream`
+ *     (NULL = the null stream) and returns.  Calls are therefore capturable in a
+ *     hipGraph.
+ *   - Arithmetic: row statistics and every output that can cancel (LayerNorm y, all
+ *     dx) are formed in fp64 and rounded once to the output type (through fp32, so a
+ *     16-bit output is at most 1 unit in the last place from the correctly rounded
+ *     value).  RMSNorm y is formed in fp32 from (float)w + offset.
+ *   - Errors: arguments are checked before any HIP call; on error nothing is enqueued
+ *     and an rn_status < 0 is returned.  RN_ERR_HIP reports a failed launch.
+ *   - Aliasing: an output may alias an input of the same shape and stride (y == x,
+ *     residual_out == residual, dx == dy or dx == dres_out: each element is read
+ *     before it is written by the same thread).  Any other overlap is undefined.
+ */
+#ifndef ROWNORM_H
+#define ROWNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rn_dtype { RN_F32 = 0, RN_F16 = 1, RN_BF16 = 2 } rn_dtype;
+
+typedef enum rn_status {
+  RN_OK = 0,
+  RN_ERR_NULL = -1,       /* a required pointer is NULL (with M > 0)              */
+  RN_ERR_SHAPE = -2,      /* M < 0, N < 1 or N > RN_MAX_N                          */
+  RN_ERR_DTYPE = -3,      /* unknown type, or a weight type other than xt / F32   */
+  RN_ERR_STRIDE = -4,     /* a row stride below N                                  */
+  RN_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than rn_bwd_workspace_bytes */
+  RN_ERR_HIP = -6,        /* a kernel launch failed                                */
+  RN_ERR_ALIAS = -7       /* two outputs share storage                             */
+} rn_status;
+
+#define RN_MAX_N 24576
+
+/* Bytes of workspace a backward call needs for `n_param_grads` (0, 1 or 2) fp32
+ * parameter gradients at this shape: per-workgroup partial rows of dw / db,
+ * reduced by a second kernel in fixed order.  0 when n_param_grads == 0 (frozen
+ * parameters need no workspace: [frozen], Motivation).  Returns 0 for invalid shapes. */
+size_t rn_bwd_workspace_bytes(int64_t M, int64_t N, int n_param_grads);
+
+/* RMSNorm forward.  [gemma] Summary: offset added to the weight in fp32 in-kernel.
+ *   x [M, ldx] in, w [N] in, y [M, ldy] out, rstd [M] out (fp32, may be NULL when no
+ *   backward follows).  eps >= 0. */
+int rmsnorm_fwd(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
+                float* rstd, int64_t M, int64_t N, float eps, float offset,
+                rn_dtype xt, rn_dtype wt, hipStream_t stream);
+
+/* RMSNorm backward.  [frozen] Key Changes (RMSNorm dW pruned when frozen);
+ * [gemma] Summary (offset applied in the backward too).
+ *   dy [M, lddy] in, x [M, ldx] in (the forward's input), w [N] in,
+ *   dx [M, lddx] out (may equal dy), dw [N] fp32 out or NULL (frozen weight: no
+ *   workspace, no partials, no second kernel), ws / ws_bytes: workspace of at least
+ *   rn_bwd_workspace_bytes(M, N, dw != NULL) bytes (may be NULL / 0 when dw is NULL).
+ *   The row statistics are recomputed from x in fp64 (no saved rstd is taken). */
+int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
+                void* dx, int64_t lddx, float* dw, void* ws, size_t ws_bytes,
+                int64_t M, int64_t N, float eps, float offset,
+                rn_dtype xt, rn_dtype wt, hipStream_t stream);
+
+/* LayerNorm forward.  [frozen] Key Changes (LayerNorm with weight and bias).
+ *   x in, w [N] in, b [N] in or NULL (no bias), y out, mean / rstd [M] fp32 out or
+ *   NULL.  eps >= 0. */
+int layernorm_fwd(const void* x, int64_t ldx, const void* w, const void* b, void* y,
+                  int64_t ldy, float* mean, float* rstd, int64_t M, int64_t N, float eps,
+                  rn_dtype xt, rn_dtype wt, hipStream_t stream);
+
+/* LayerNorm backward.  [frozen] Key Changes: dW and dB are pruned independently.
+ *   dw, db: fp32 [N] out, each may be NULL.  Workspace of at least
+ *   rn_bwd_workspace_bytes(M, N, (dw != NULL) + (db != NULL)) bytes. */
+int layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
+                  void* dx, int64_t lddx, float* dw, float* db, void* ws, size_t ws_bytes,
+                  int64_t M, int64_t N, float eps, rn_dtype xt, rn_dtype wt,
+                  hipStream_t stream);
+
+/* FusedAddRMSNorm forward.  [gemma] Summary (Gemma offset on this op),
+ * PyTorch accuracy comparison (the rounded sum is what is saved).
+ *   x, residual in; residual_out = round(x + residual) out (may equal residual);
+ *   y out; rstd [M] fp32 out or NULL. */
+int fused_add_rmsnorm_fwd(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                          const void* w, void* y, int64_t ldy, void* residual_out,
+                          int64_t ldro, float* rstd, int64_t M, int64_t N, float eps,
+                          float offset, rn_dtype xt, rn_dtype wt, hipStream_t stream);
+
+/* FusedAddRMSNorm backward.  [gemma] PyTorch accuracy comparison (residual-output
+ * gradient; the backward works from the rounded saved residual).
+ *   dy in; dres_out in or NULL (no gradient reaches residual_out); residual_out in
+ *   (the forward's output); dx out = gradient of x and of residual (may equal dy or
+ *   dres_out); dw fp32 out or NULL; workspace as for rmsnorm_bwd. */
+int fused_add_rmsnorm_bwd(const void* dy, int64_t lddy, const void* dres_out, int64_t lddr,
+                          const void* residual_out, int64_t ldro, const void* w, void* dx,
+                          int64_t lddx, float* dw, void* ws, size_t ws_bytes, int64_t M,
+                          int64_t N, float eps, float offset, rn_dtype xt, rn_dtype wt,
+                          hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* rn_status_str(int status);
+
+/* Launch-shape override for tuning sweeps (0 = automatic for every field).
+ *   kind 0 = forward kernels, 1 = backward kernels with parameter gradients,
+ *   2 = backward kernels without them.  v: elements per thread per row (one of the
+ *   compiled sizes), rows: rows per workgroup pass, wg_rows: rows per workgroup in
+ *   total (backward partial-row granularity).  Process-wide; not thread-safe; a
+ *   shape that cannot run the problem is ignored.  Returns RN_OK or RN_ERR_SHAPE. */
+int rn_set_launch_override(int kind, int v, int rows, int wg_rows);
+
+/* Instrumentation for timing the two backward stages separately.  While `ev` is not
+ * NULL, every backward call that computes parameter gradients records `ev` on its
+ * stream between its first kernel (dx and partial rows) and its column-sum kernel.
+ * Pass NULL to stop.  Process-wide; not thread-safe.  Always returns RN_OK. */
+int rn_set_stage_event(hipEvent_t ev);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ROWNORM_H */

@@ -1,0 +1,357 @@
+// rn_abi.hip — the C ABI (include/rownorm.h): argument checks, launch shapes and
+// dispatch to the kernel instances.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/rownorm.h"
+#include "rn_launch.h"
+
+namespace rn {
+
+// ------------------------------------------------------------------------------------
+// Backward, stage 2: out[j] = sum over p = 0..P-1 of partial[p][j], in a fixed order
+// (thread slice s sums p = s, s + S, ... ascending; slices are then added in s order),
+// so dw / db are bitwise reproducible.  blockIdx.y picks dw (0) or db (1).
+// ------------------------------------------------------------------------------------
+constexpr int CS_THREADS = 256;
+constexpr int CS_C4 = 16;                 // float4 columns per workgroup (64 columns)
+constexpr int CS_S = CS_THREADS / CS_C4;  // row slices per workgroup
+
+__global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const float* ws, int64_t ldws, int P,
+                                                            int N, float* out0, float* out1) {
+  __shared__ float4 sh[CS_S][CS_C4];
+  const float* src = ws + (blockIdx.y ? static_cast<int64_t>(P) * ldws : 0);
+  float* out = blockIdx.y ? out1 : out0;
+  const int ci = threadIdx.x % CS_C4;
+  const int s = threadIdx.x / CS_C4;
+  const int c = (blockIdx.x * CS_C4 + ci) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < N) {
+    for (int q = s; q < P; q += CS_S) {
+      const float4 v = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(q) * ldws + c);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+  }
+  sh[s][ci] = acc;
+  __syncthreads();
+  if (s == 0 && c < N) {
+    float4 tot = sh[0][ci];
+    for (int q = 1; q < CS_S; ++q) {
+      const float4 v = sh[q][ci];
+      tot.x += v.x;
+      tot.y += v.y;
+      tot.z += v.z;
+      tot.w += v.w;
+    }
+    out[c] = tot.x;
+    if (c + 1 < N) out[c + 1] = tot.y;
+    if (c + 2 < N) out[c + 2] = tot.z;
+    if (c + 3 < N) out[c + 3] = tot.w;
+  }
+}
+
+}  // namespace rn
+
+using namespace rn;
+
+namespace {
+
+// At most this many partial rows per parameter gradient.  The row-to-workgroup split
+// depends only on (M, N), never on the device, so dw / db are bitwise reproducible.
+constexpr int64_t kMaxPartials = 256;
+// Dynamic LDS budget of the stage-1 team combine.
+constexpr size_t kMaxCombineLds = 60 * 1024;  // + 1 KiB of reduction slots < 64 KiB
+
+struct Override {
+  int v = 0, rows = 0, wg_rows = 0;
+};
+Override g_override[3];  // 0: forward, 1: backward with grads, 2: backward without
+hipEvent_t g_stage_event = nullptr;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline int64_t ldws_of(int64_t N) { return round_up(N, 64); }
+
+inline bool valid_dtype(int t) { return t == RN_F32 || t == RN_F16 || t == RN_BF16; }
+inline int elem_bytes(int t) { return t == RN_F32 ? 4 : 2; }
+inline int to_dt(int t) { return t == RN_F32 ? DT_F32 : (t == RN_F16 ? DT_F16 : DT_BF16); }
+
+inline int check_types(rn_dtype xt, rn_dtype wt) {
+  if (!valid_dtype(xt) || !valid_dtype(wt)) return RN_ERR_DTYPE;
+  if (wt != xt && wt != RN_F32) return RN_ERR_DTYPE;
+  return RN_OK;
+}
+
+inline int check_shape(int64_t M, int64_t N) {
+  if (M < 0 || N < 1 || N > RN_MAX_N) return RN_ERR_SHAPE;
+  if (M > (int64_t(1) << 40)) return RN_ERR_SHAPE;
+  if (M * N > (int64_t(1) << 46)) return RN_ERR_SHAPE;
+  return RN_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A row tensor allows 16-byte accesses if its base and (for M > 1) its row pitch are
+// 16-byte multiples.  Null tensors (optional and absent) do not constrain.
+inline bool vec_ok(const void* p, int64_t ld, int64_t M, int eb) {
+  if (p == nullptr) return true;
+  if (!aligned16(p)) return false;
+  return M <= 1 || ((ld * eb) % 16) == 0;
+}
+
+// Smallest compiled V whose team (ceil(N / V) rounded up to whole waves) fits the
+// kernel's workgroup limit, starting from a preferred V.
+inline int pick_v(int64_t N, int preferred) {
+  for (int v : kVs) {
+    if (v < preferred) continue;
+    const int64_t team = round_up(cdiv(N, v), 64);
+    if (team <= max_wg(v)) return v;
+  }
+  return 0;
+}
+
+struct Shape {
+  int v = 0;
+  int team = 0;
+  int R = 1;               // teams per workgroup
+  int64_t rows_per_wg = 1;
+  int64_t grid = 0;
+  int P = 0;               // partial rows (backward with grads)
+  size_t shmem = 0;
+};
+
+// kind: 0 forward, 1 backward with parameter grads, 2 backward without.
+Shape plan(int kind, int64_t M, int64_t N, int xt) {
+  Shape s;
+  const Override& o = g_override[kind];
+  // Default elements per thread: forward 16, backward 8 (the backward holds two
+  // input rows plus fp32 accumulators per element).
+  const int pref = kind == 0 ? 16 : 8;
+  s.v = pick_v(N, o.v ? o.v : pref);
+  if (s.v == 0) s.v = pick_v(N, pref);
+  if (s.v == 0) s.v = pick_v(N, 8);
+  s.team = static_cast<int>(round_up(cdiv(N, s.v), 64));
+  const int wg_cap = max_wg(s.v);
+  // Teams per workgroup: about 256 threads by default.
+  int R = o.rows ? o.rows : std::max(1, 256 / s.team);
+  R = std::max(1, std::min(R, wg_cap / s.team));
+  if (kind == 1) {
+    while (R > 1 && static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) > kMaxCombineLds) --R;
+  }
+  s.R = R;
+  if (kind == 1) {
+    const int64_t groups = cdiv(M, R);
+    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : cdiv(groups, kMaxPartials) * R;
+    if (cdiv(M, rows) > std::min<int64_t>(M, kMaxPartials)) rows = cdiv(groups, kMaxPartials) * R;
+    s.rows_per_wg = std::max<int64_t>(rows, R);
+    s.P = static_cast<int>(M > 0 ? cdiv(M, s.rows_per_wg) : 0);
+    s.grid = s.P;
+    s.shmem = R > 1 ? static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) : 0;
+  } else {
+    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : R;
+    // keep the grid within the 2^31 workgroup limit for very tall inputs
+    rows = std::max<int64_t>(rows, round_up(cdiv(M, int64_t(1) << 30), R));
+    s.rows_per_wg = std::max<int64_t>(rows, R);
+    s.grid = M > 0 ? cdiv(M, s.rows_per_wg) : 0;
+  }
+  (void)xt;
+  return s;
+}
+
+inline int launched() { return hipGetLastError() == hipSuccess ? RN_OK : RN_ERR_HIP; }
+
+int colsum(const float* ws, int64_t ldws, int P, int64_t N, float* o0, float* o1,
+           hipStream_t st) {
+  const int n_out = (o0 != nullptr) + (o1 != nullptr);
+  if (n_out == 0) return RN_OK;
+  dim3 grid(static_cast<unsigned>(cdiv(N, CS_C4 * 4)), n_out);
+  colsum_kernel<<<grid, CS_THREADS, 0, st>>>(ws, ldws, P, static_cast<int>(N),
+                                             o0 != nullptr ? o0 : o1, o1);
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rn_bwd_workspace_bytes(int64_t M, int64_t N, int n_param_grads) {
+  if (check_shape(M, N) != RN_OK || n_param_grads <= 0 || n_param_grads > 2) return 0;
+  return static_cast<size_t>(n_param_grads) * static_cast<size_t>(std::min(M, kMaxPartials)) *
+         static_cast<size_t>(ldws_of(N)) * sizeof(float);
+}
+
+const char* rn_status_str(int status) {
+  switch (status) {
+    case RN_OK: return "ok";
+    case RN_ERR_NULL: return "a required pointer is NULL";
+    case RN_ERR_SHAPE: return "invalid shape (need M >= 0 and 1 <= N <= RN_MAX_N)";
+    case RN_ERR_DTYPE: return "invalid dtype (weight type must equal the I/O type or be F32)";
+    case RN_ERR_STRIDE: return "a row stride is smaller than N";
+    case RN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case RN_ERR_HIP: return "kernel launch failed";
+    case RN_ERR_ALIAS: return "two outputs share storage";
+    default: return "unknown status";
+  }
+}
+
+int rn_set_launch_override(int kind, int v, int rows, int wg_rows) {
+  if (kind < 0 || kind > 2 || v < 0 || rows < 0 || wg_rows < 0) return RN_ERR_SHAPE;
+  if (v != 0) {
+    bool known = false;
+    for (int k : kVs) known = known || (k == v);
+    if (!known) return RN_ERR_SHAPE;
+  }
+  g_override[kind].v = v;
+  g_override[kind].rows = rows;
+  g_override[kind].wg_rows = wg_rows;
+  return RN_OK;
+}
+
+int rn_set_stage_event(hipEvent_t ev) {
+  g_stage_event = ev;
+  return RN_OK;
+}
+
+// ---------------------------------------------------------------------------- forward
+
+static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t ldr,
+                   const void* w, const void* b, void* y, int64_t ldy, void* ro, int64_t ldro,
+                   float* rstd, float* mean, int64_t M, int64_t N, float eps, float offset,
+                   rn_dtype xt, rn_dtype wt, hipStream_t st) {
+  int e = check_types(xt, wt);
+  if (e != RN_OK) return e;
+  if ((e = check_shape(M, N)) != RN_OK) return e;
+  if (M == 0) return RN_OK;
+  if (x == nullptr || w == nullptr || y == nullptr) return RN_ERR_NULL;
+  if (op == OP_FADD && (res == nullptr || ro == nullptr)) return RN_ERR_NULL;
+  if (M > 1 && (ldx < N || ldy < N)) return RN_ERR_STRIDE;
+  if (op == OP_FADD && M > 1 && (ldr < N || ldro < N)) return RN_ERR_STRIDE;
+  if (op == OP_FADD && ro == y) return RN_ERR_ALIAS;
+  if ((rstd != nullptr && rstd == mean)) return RN_ERR_ALIAS;
+
+  const int eb = elem_bytes(xt);
+  const int ve = 16 / eb;
+  bool vec = (N % ve) == 0 && vec_ok(x, ldx, M, eb) && vec_ok(y, ldy, M, eb) &&
+             aligned16(w) && (b == nullptr || aligned16(b));
+  if (op == OP_FADD) vec = vec && vec_ok(res, ldr, M, eb) && vec_ok(ro, ldro, M, eb);
+
+  const Shape s = plan(0, M, N, xt);
+  FwdArgs a{};
+  a.x = x; a.ldx = ldx; a.res = res; a.ldr = ldr; a.w = w; a.b = b;
+  a.y = y; a.ldy = ldy; a.ro = ro; a.ldro = ldro; a.rstd = rstd; a.mean = mean;
+  a.M = M; a.N = static_cast<int>(N); a.team = s.team;
+  a.rows_per_wg = static_cast<int>(s.rows_per_wg);
+  a.eps = eps; a.offset = offset;
+  Launch l{s.v, vec, dim3(static_cast<unsigned>(s.grid)), dim3(static_cast<unsigned>(s.R * s.team)),
+           0};
+  bool ok = false;
+  const int dx = to_dt(xt), dw = to_dt(wt);
+  if (op == OP_RMS) ok = launch_fwd_rms(dx, dw, l, a, st);
+  else if (op == OP_LN) ok = launch_fwd_ln(dx, dw, l, a, st);
+  else ok = launch_fwd_fadd(dx, dw, l, a, st);
+  if (!ok) return RN_ERR_DTYPE;
+  return launched();
+}
+
+int rmsnorm_fwd(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd,
+                int64_t M, int64_t N, float eps, float offset, rn_dtype xt, rn_dtype wt,
+                hipStream_t stream) {
+  return forward(OP_RMS, x, ldx, nullptr, 0, w, nullptr, y, ldy, nullptr, 0, rstd, nullptr, M, N,
+                 eps, offset, xt, wt, stream);
+}
+
+int layernorm_fwd(const void* x, int64_t ldx, const void* w, const void* b, void* y, int64_t ldy,
+                  float* mean, float* rstd, int64_t M, int64_t N, float eps, rn_dtype xt,
+                  rn_dtype wt, hipStream_t stream) {
+  return forward(OP_LN, x, ldx, nullptr, 0, w, b, y, ldy, nullptr, 0, rstd, mean, M, N, eps, 0.0f,
+                 xt, wt, stream);
+}
+
+int fused_add_rmsnorm_fwd(const void* x, int64_t ldx, const void* residual, int64_t ldr,
+                          const void* w, void* y, int64_t ldy, void* residual_out, int64_t ldro,
+                          float* rstd, int64_t M, int64_t N, float eps, float offset, rn_dtype xt,
+                          rn_dtype wt, hipStream_t stream) {
+  return forward(OP_FADD, x, ldx, residual, ldr, w, nullptr, y, ldy, residual_out, ldro, rstd,
+                 nullptr, M, N, eps, offset, xt, wt, stream);
+}
+
+// --------------------------------------------------------------------------- backward
+
+static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                    const void* dres, int64_t lddr, const void* w, void* dx, int64_t lddx,
+                    float* dw, float* db, void* ws, size_t ws_bytes, int64_t M, int64_t N,
+                    float eps, float offset, rn_dtype xt, rn_dtype wt, hipStream_t st) {
+  int e = check_types(xt, wt);
+  if (e != RN_OK) return e;
+  if ((e = check_shape(M, N)) != RN_OK) return e;
+  const int ngrads = (dw != nullptr) + (db != nullptr);
+  if (dw != nullptr && dw == db) return RN_ERR_ALIAS;
+  if (ngrads > 0) {
+    const size_t need = rn_bwd_workspace_bytes(M, N, ngrads);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return RN_ERR_WORKSPACE;
+  }
+  if (M > 0) {
+    if (dy == nullptr || x == nullptr || w == nullptr || dx == nullptr) return RN_ERR_NULL;
+    if (M > 1 && (lddy < N || ldx < N || lddx < N)) return RN_ERR_STRIDE;
+    if (dres != nullptr && M > 1 && lddr < N) return RN_ERR_STRIDE;
+  }
+  const int64_t ldws = ldws_of(N);
+  if (M == 0) {  // parameter gradients of an empty batch are zero
+    return colsum(static_cast<const float*>(ws), ldws, 0, N, dw, db, st);
+  }
+
+  const int eb = elem_bytes(xt);
+  const int ve = 16 / eb;
+  const bool vec = (N % ve) == 0 && vec_ok(dy, lddy, M, eb) && vec_ok(x, ldx, M, eb) &&
+                   vec_ok(dx, lddx, M, eb) && vec_ok(dres, lddr, M, eb) && aligned16(w);
+
+  const Shape s = plan(ngrads > 0 ? 1 : 2, M, N, xt);
+  BwdArgs a{};
+  a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
+  a.dx = dx; a.lddx = lddx;
+  a.ws = static_cast<float*>(ws); a.ldws = ldws; a.P = s.P;
+  a.M = M; a.N = static_cast<int>(N); a.team = s.team;
+  a.rows_per_wg = static_cast<int>(s.rows_per_wg);
+  a.eps = eps; a.offset = offset;
+  Launch l{s.v, vec, dim3(static_cast<unsigned>(s.grid)), dim3(static_cast<unsigned>(s.R * s.team)),
+           s.shmem};
+  bool ok = false;
+  const int dxt = to_dt(xt), dwt = to_dt(wt);
+  if (op == OP_RMS) ok = launch_bwd_rms(dxt, dwt, dw != nullptr, l, a, st);
+  else if (op == OP_LN) ok = launch_bwd_ln(dxt, dwt, dw != nullptr, db != nullptr, l, a, st);
+  else ok = launch_bwd_fadd(dxt, dwt, dw != nullptr, l, a, st);
+  if (!ok) return RN_ERR_DTYPE;
+  if ((e = launched()) != RN_OK) return e;
+  if (ngrads == 0) return RN_OK;  // frozen: no partials, no second kernel
+  if (g_stage_event != nullptr && hipEventRecord(g_stage_event, st) != hipSuccess) return RN_ERR_HIP;
+  return colsum(static_cast<const float*>(ws), ldws, s.P, N, dw, db, st);
+}
+
+int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, void* dx,
+                int64_t lddx, float* dw, void* ws, size_t ws_bytes, int64_t M, int64_t N, float eps,
+                float offset, rn_dtype xt, rn_dtype wt, hipStream_t stream) {
+  return backward(OP_RMS, dy, lddy, x, ldx, nullptr, 0, w, dx, lddx, dw, nullptr, ws, ws_bytes, M,
+                  N, eps, offset, xt, wt, stream);
+}
+
+int layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, void* dx,
+                  int64_t lddx, float* dw, float* db, void* ws, size_t ws_bytes, int64_t M,
+                  int64_t N, float eps, rn_dtype xt, rn_dtype wt, hipStream_t stream) {
+  return backward(OP_LN, dy, lddy, x, ldx, nullptr, 0, w, dx, lddx, dw, db, ws, ws_bytes, M, N,
+                  eps, 0.0f, xt, wt, stream);
+}
+
+int fused_add_rmsnorm_bwd(const void* dy, int64_t lddy, const void* dres_out, int64_t lddr,
+                          const void* residual_out, int64_t ldro, const void* w, void* dx,
+                          int64_t lddx, float* dw, void* ws, size_t ws_bytes, int64_t M, int64_t N,
+                          float eps, float offset, rn_dtype xt, rn_dtype wt, hipStream_t stream) {
+  return backward(OP_FADD, dy, lddy, residual_out, ldro, dres_out, lddr, w, dx, lddx, dw, nullptr,
+                  ws, ws_bytes, M, N, eps, offset, xt, wt, stream);
+}
+
+}  // extern "C"

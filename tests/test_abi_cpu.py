@@ -1,0 +1,123 @@
+"""CPU-side checks of the C ABI: the library loads without a GPU, exports every
+function include/rownorm.h declares, and rejects bad arguments with the documented
+status codes before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rownorm.h")
+
+
+@pytest.fixture(scope="module")
+def rn():
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import normalization_row_wise_amd as rn
+    return rn
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"#[^\n]*", "", text)
+    names = re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{}]*\)\s*;", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_six_operations():
+    names = declared_functions()
+    for n in ("rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+              "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_bwd", "rn_bwd_workspace_bytes",
+              "rn_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(rn):
+    lib = ctypes.CDLL(rn.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+F32, F16, BF16 = 0, 1, 2
+P = ctypes.c_void_p(4096)    # a non-null address that is never dereferenced
+Q = ctypes.c_void_p(8192)
+Rr = ctypes.c_void_p(12288)
+S = ctypes.c_void_p(16384)
+
+
+def test_status_strings(rn):
+    for code in (RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS):
+        s = rn.lib.rn_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert rn.lib.rn_status_str(42).decode() == "unknown status"
+
+
+def test_workspace_query(rn):
+    ws = rn.workspace_bytes
+    assert ws(2048, 4096, 0) == 0              # frozen: nothing
+    assert ws(0, 4096, 1) == 0                 # empty batch: nothing to stage
+    one = ws(2048, 4096, 1)
+    assert one > 0 and ws(2048, 4096, 2) == 2 * one
+    assert one % 16 == 0 and one >= 4096 * 4
+    assert ws(8192, 8192, 1) >= ws(2048, 4096, 1)
+    assert ws(-1, 4096, 1) == 0 and ws(4, 0, 1) == 0 and ws(4, 10**6, 1) == 0
+    assert ws(4, 64, 3) == 0
+
+
+def test_forward_argument_errors(rn):
+    L = rn.lib
+    f = L.rmsnorm_fwd
+    assert f(P, 64, Q, Rr, 64, None, 0, 64, 1e-6, 0.0, BF16, BF16, None) == RN_OK   # M = 0: no-op
+    assert f(P, 64, Q, Rr, 64, None, 4, 64, 1e-6, 0.0, 7, BF16, None) == E_DTYPE
+    assert f(P, 64, Q, Rr, 64, None, 4, 64, 1e-6, 0.0, BF16, F16, None) == E_DTYPE  # mixed 16-bit
+    assert f(P, 64, Q, Rr, 64, None, -1, 64, 1e-6, 0.0, BF16, BF16, None) == E_SHAPE
+    assert f(P, 64, Q, Rr, 64, None, 4, 0, 1e-6, 0.0, BF16, BF16, None) == E_SHAPE
+    assert f(P, 99999, Q, Rr, 99999, None, 4, 99999, 1e-6, 0.0, BF16, BF16, None) == E_SHAPE
+    assert f(None, 64, Q, Rr, 64, None, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_NULL
+    assert f(P, 64, None, Rr, 64, None, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_NULL
+    assert f(P, 63, Q, Rr, 64, None, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_STRIDE
+    assert f(P, 64, Q, Rr, 32, None, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_STRIDE
+    g = L.layernorm_fwd
+    assert g(P, 64, Q, None, Rr, 64, S, S, 4, 64, 1e-5, F32, F32, None) == E_ALIAS
+    assert g(P, 64, None, None, Rr, 64, None, None, 4, 64, 1e-5, F32, F32, None) == E_NULL
+    h = L.fused_add_rmsnorm_fwd
+    assert h(P, 64, None, 64, Q, Rr, 64, S, 64, None, 4, 64, 1e-6, 1.0, BF16, BF16, None) == E_NULL
+    assert h(P, 64, P, 64, Q, Rr, 64, Rr, 64, None, 4, 64, 1e-6, 1.0, BF16, BF16, None) == E_ALIAS
+    assert h(P, 64, P, 16, Q, Rr, 64, S, 64, None, 4, 64, 1e-6, 1.0, BF16, BF16, None) == E_STRIDE
+
+
+def test_backward_argument_errors(rn):
+    L = rn.lib
+    b = L.rmsnorm_bwd
+    need = rn.workspace_bytes(4, 64, 1)
+    # workspace missing or too small while dw is requested
+    assert b(P, 64, Q, 64, Rr, S, 64, P, None, 0, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_WS
+    assert b(P, 64, Q, 64, Rr, S, 64, P, Q, need - 4, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_WS
+    assert b(P, 64, Q, 64, Rr, S, 64, P, ctypes.c_void_p(4100), need, 4, 64, 1e-6, 0.0, BF16,
+             BF16, None) == E_WS                                   # misaligned workspace
+    assert b(None, 64, Q, 64, Rr, S, 64, None, None, 0, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_NULL
+    assert b(P, 64, Q, 64, Rr, None, 64, None, None, 0, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_NULL
+    assert b(P, 8, Q, 64, Rr, S, 64, None, None, 0, 4, 64, 1e-6, 0.0, BF16, BF16, None) == E_STRIDE
+    assert b(P, 64, Q, 64, Rr, S, 64, None, None, 0, 4, 64, 1e-6, 0.0, F16, BF16, None) == E_DTYPE
+    ln = L.layernorm_bwd
+    assert ln(P, 64, Q, 64, Rr, S, 64, P, P, Q, 1 << 20, 4, 64, 1e-5, F32, F32, None) == E_ALIAS
+    need2 = rn.workspace_bytes(4, 64, 2)
+    assert ln(P, 64, Q, 64, Rr, S, 64, P, Q, Rr, need2 - 16, 4, 64, 1e-5, F32, F32, None) == E_WS
+    fa = L.fused_add_rmsnorm_bwd
+    assert fa(P, 64, None, 0, None, 64, Rr, S, 64, None, None, 0, 4, 64, 1e-6, 1.0, BF16, BF16,
+              None) == E_NULL                                      # residual_out missing
+    assert fa(P, 64, Q, 8, Q, 64, Rr, S, 64, None, None, 0, 4, 64, 1e-6, 1.0, BF16, BF16,
+              None) == E_STRIDE                                    # dres_out stride
+
+
+def test_launch_override_validation(rn):
+    L = rn.lib
+    assert L.rn_set_launch_override(3, 0, 0, 0) == E_SHAPE
+    assert L.rn_set_launch_override(0, 12, 0, 0) == E_SHAPE       # not a compiled V
+    assert L.rn_set_launch_override(0, 16, 2, 0) == RN_OK
+    assert L.rn_set_launch_override(0, 0, 0, 0) == RN_OK          # back to automatic

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every case prints what it is before touching the GPU, so a failing run names it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import gpu_parity as gp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+    import normalization_row_wise_amd as rn
+    return rn
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ---- the named workloads at their full sizes ----------------------------------------
+
+FULL = [c for c in workloads.CONFIGS]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda c: c.name)
+def test_named_workload(wl):
+    _say(wl.name)
+    sample = 512 if wl.M * wl.N > 16 * 2**20 else None
+    fails = gp.check(wl, sample_rows=sample)
+    assert not fails, "\n".join(fails)
+
+
+# ---- ragged shapes, several tiles, every type pair -----------------------------------
+
+RAGGED_N = [1, 7, 64, 100, 511, 512, 513, 1000, 1024, 2050, 4095, 4096, 4097, 8191, 8193,
+            12288, 16383, 16385, 18432, 24576]
+TYPES = [("bf16", "bf16"), ("fp16", "fp16"), ("fp32", "fp32"), ("bf16", "fp32"), ("fp16", "fp32")]
+OPS = ["rmsnorm", "layernorm", "fused_add_rmsnorm"]
+
+
+def _cases():
+    out = []
+    for i, n in enumerate(RAGGED_N):
+        for j, (io, wt) in enumerate(TYPES):
+            op = OPS[(i + j) % 3]
+            m = [1, 3, 37, 130][(i + 2 * j) % 4]
+            off = 1.0 if op != "layernorm" and (i + j) % 2 else 0.0
+            out.append(workloads.small(op, m, n, io, wt, offset=off,
+                                       weight="gemma" if off else "unit", seed=100 + 7 * i + j))
+    return out
+
+
+@pytest.mark.parametrize("wl", _cases(), ids=lambda c: c.name)
+def test_ragged(wl):
+    _say(wl.name)
+    fails = gp.check(wl)
+    assert not fails, "\n".join(fails)
+
+
+# ---- frozen parameters ----------------------------------------------------------------
+
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("io", ["bf16", "fp32"])
+def test_frozen_dx_bit_identical_and_dw_unchanged(op, io):
+    import normalization_row_wise_amd as rn
+    wl = workloads.small(op, 300, 4096, io, offset=1.0 if op != "layernorm" else 0.0, seed=5)
+    _say("frozen", wl.name)
+    t = workloads.generate(wl)
+    full = gp.run_gpu(wl, t, dw=True, db=True)
+    frozen = gp.run_gpu(wl, t, dw=False, db=False)
+    assert torch.equal(full["dx"].view(torch.int16 if io != "fp32" else torch.int32),
+                       frozen["dx"].view(torch.int16 if io != "fp32" else torch.int32))
+    assert frozen["dw"] is None
+    if op == "layernorm":
+        only_w = gp.run_gpu(wl, t, dw=True, db=False)
+        only_b = gp.run_gpu(wl, t, dw=False, db=True)
+        assert only_w["db"] is None and only_b["dw"] is None
+        assert torch.equal(only_w["dw"], full["dw"]) and torch.equal(only_b["db"], full["db"])
+        for r in (only_w, only_b):
+            assert torch.equal(r["dx"].view(torch.int32 if io == "fp32" else torch.int16),
+                               full["dx"].view(torch.int32 if io == "fp32" else torch.int16))
+    # dw is reproducible bit for bit
+    again = gp.run_gpu(wl, t, dw=True, db=True)
+    assert torch.equal(again["dw"], full["dw"])
+    del rn
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "fused_add_rmsnorm"])
+def test_dw_independent_of_offset(op):
+    # the offset is a constant of the weight: dw must not move with it
+    import normalization_row_wise_amd as rn
+    _say("offset-independence", op)
+    wl1 = workloads.small(op, 128, 4096, "bf16", offset=1.0, weight="gemma", seed=9)
+    wl0 = workloads.small(op, 128, 4096, "bf16", offset=0.0, weight="gemma", seed=9)
+    g1 = gp.run_gpu(wl1, workloads.generate(wl1))
+    g0 = gp.run_gpu(wl0, workloads.generate(wl0))
+    assert torch.equal(g1["dw"], g0["dw"])
+    assert not torch.equal(g1["dx"], g0["dx"])
+    del rn
+
+
+# ---- layouts: strided rows, in-place backward, empty batch ------------------------------
+
+@pytest.mark.parametrize("io", ["bf16", "fp16", "fp32"])
+def test_strided_rows_and_inplace_backward(io):
+    import normalization_row_wise_amd as rn
+    _say("strided+inplace", io)
+    M, N, pad = 67, 1000, 24
+    wl = workloads.small("rmsnorm", M, N, io, offset=1.0, weight="gemma", seed=11)
+    t = workloads.generate(wl)
+    o = gp.run_oracle(wl, t)
+    td = workloads.TORCH_DTYPES[io]
+    big = torch.zeros(M, N + pad, dtype=td, device=gp.dev())
+    x = big[:, 3:3 + N]
+    x.copy_(t["x"].to(gp.dev()))
+    gbig = torch.zeros(M, N + 2 * pad, dtype=td, device=gp.dev())
+    dy = gbig[:, 5:5 + N]
+    dy.copy_(t["dy"].to(gp.dev()))
+    w = t["w"].to(gp.dev())
+    ybig = torch.full((M, N + pad), 7.0, dtype=td, device=gp.dev())
+    y, _ = rn.rmsnorm_fwd(x, w, t["eps"], t["offset"], y=ybig[:, 1:1 + N])
+    dx, dw = rn.rmsnorm_bwd(dy, x, w, t["eps"], t["offset"], dx=dy)   # in place over dy
+    torch.cuda.synchronize()
+    assert dx.data_ptr() == dy.data_ptr()
+    for k, g in (("y", y), ("dx", dx)):
+        rep = gp.io_report(g.cpu(), o[k], io)
+        assert gp.io_ok(rep, io), (k, rep)
+    assert gp.f32_report(dw.cpu(), o["dw"]) <= gp.REL_GRAD
+    # padding untouched
+    assert torch.all(ybig[:, 0] == 7.0) and torch.all(ybig[:, 1 + N:] == 7.0)
+
+
+def test_fused_add_inplace_residual_and_layernorm_without_bias():
+    import normalization_row_wise_amd as rn
+    _say("fused-add in place / layernorm no bias")
+    wl = workloads.small("fused_add_rmsnorm", 40, 2048, "bf16", offset=1.0, weight="gemma", seed=12)
+    t = workloads.generate(wl)
+    o = gp.run_oracle(wl, t)
+    d = gp.to_device(t)
+    res = d["residual"].clone()
+    y, ro, _ = rn.fused_add_rmsnorm_fwd(d["x"], res, d["w"], t["eps"], t["offset"], residual_out=res)
+    dres = d["dres"].clone()
+    dx, _ = rn.fused_add_rmsnorm_bwd(d["dy"], ro, d["w"], t["eps"], t["offset"], dres, dx=dres,
+                                     dw=None)
+    torch.cuda.synchronize()
+    assert ro.data_ptr() == res.data_ptr()
+    for k, g in (("y", y), ("residual_out", ro), ("dx", dx)):
+        rep = gp.io_report(g.cpu(), o[k], "bf16")
+        assert gp.io_ok(rep, "bf16"), (k, rep)
+    wl = workloads.small("layernorm", 33, 3000, "bf16", bias=False, seed=13)
+    fails = gp.check(wl)
+    assert not fails, fails
+
+
+def test_empty_batch_gives_zero_parameter_gradients():
+    import normalization_row_wise_amd as rn
+    _say("M = 0")
+    x = torch.empty(0, 512, dtype=torch.bfloat16, device=gp.dev())
+    w = torch.ones(512, dtype=torch.bfloat16, device=gp.dev())
+    dw = torch.full((512,), 3.0, device=gp.dev())
+    db = torch.full((512,), 3.0, device=gp.dev())
+    rn.layernorm_bwd(x, x, w, 1e-5, dx=x, dw=dw, db=db)
+    y, _ = rn.rmsnorm_fwd(x, w)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0) and torch.all(db == 0) and y.shape == (0, 512)
+
+
+# ---- rounding of the packed converts: ties go to even -----------------------------------
+
+@pytest.mark.parametrize("io", ["bf16", "fp16"])
+def test_residual_rounding_ties_to_even(io):
+    import normalization_row_wise_amd as rn
+    _say("ties", io)
+    td = workloads.TORCH_DTYPES[io]
+    p = 8 if io == "bf16" else 11
+    M, N = 4, 4096
+    rng = np.random.default_rng(21)
+    # x = k * 2^e (p significant bits), r = 2^(e-p): x + r is halfway between two values
+    mant = rng.integers(2**(p - 1), 2**p, size=(M, N)).astype(np.float64)
+    e = rng.integers(-4, 4, size=(M, N)).astype(np.float64)
+    x64 = mant * 2.0 ** (e - (p - 1)) * np.where(rng.random((M, N)) < 0.5, -1, 1)
+    r64 = np.sign(x64) * 2.0 ** (e - p)
+    r64[:, ::3] = -r64[:, ::3]
+    x = torch.tensor(x64, dtype=torch.float32).to(td)
+    r = torch.tensor(r64, dtype=torch.float32).to(td)
+    assert np.array_equal(x.double().numpy(), x64) and np.array_equal(r.double().numpy(), r64)
+    w = torch.ones(N, dtype=td)
+    _, ro, _ = rn.fused_add_rmsnorm_fwd(x.to(gp.dev()), r.to(gp.dev()), w.to(gp.dev()), 1e-6, 0.0)
+    torch.cuda.synchronize()
+    ref = oracle.round_to(x64 + r64, io)
+    assert np.array_equal(gp.gpu_bits(ro.cpu(), io), oracle.to_bits(ref, io))
+
+
+def test_gemma_worked_example_on_gpu():
+    import normalization_row_wise_amd as rn
+    from tests.golden import load
+    g = load("gemma_rmsnorm_row.txt")
+    _say("gemma worked example")
+    n = int(g["n"])
+    x = torch.zeros(1, n, dtype=torch.bfloat16, device=gp.dev())
+    x[0, 0] = g["x0"]
+    w = torch.full((n,), g["w"], dtype=torch.bfloat16, device=gp.dev())
+    y, _ = rn.rmsnorm_fwd(x, w, g["eps"], g["offset"])
+    x32 = torch.ones(1, 1, device=gp.dev())
+    y32, _ = rn.rmsnorm_fwd(x32, torch.full((1,), g["w"], device=gp.dev()), 0.0, g["offset"])
+    torch.cuda.synchronize()
+    assert y[0, 0].item() == g["y0_bf16"]
+    assert y32[0, 0].item() == g["fp32_y_n1"]
+
+
+def test_errors_do_not_launch_on_device():
+    import normalization_row_wise_amd as rn
+    _say("error statuses")
+    x = torch.zeros(4, 64, dtype=torch.bfloat16, device=gp.dev())
+    w = torch.ones(64, dtype=torch.float16, device=gp.dev())
+    with pytest.raises(rn.RowNormError):
+        rn.rmsnorm_fwd(x, w)            # bf16 activations with an fp16 weight
+    ws = torch.empty(8, dtype=torch.uint8, device=gp.dev())
+    with pytest.raises(rn.RowNormError):
+        rn.rmsnorm_bwd(x, x, w.to(torch.bfloat16), workspace=ws)
