@@ -160,10 +160,14 @@ def time_steps(sets, K, W, use_graph, torch):
 
 def event_times(sets, n, rn, torch):
     """Per-kernel device time (us) from HIP events on the launch stream: forward,
-    backward stage 1 (dx + partials) and the whole backward call."""
+    backward stage 1 (dx + partials) and the whole backward call.  A spin kernel
+    holds the GPU while the host enqueues every step, so the GPU then runs them back
+    to back and the events time kernels, not host launch gaps."""
     st = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
     trainable = sets.sets[0]["dw"] is not None or sets.sets[0]["db"] is not None
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * n)))   # ~ 2 ms + 40 us per step
     for k in range(n):
         e0, e1, e2, e3 = ev[k]
         e0.record(st)

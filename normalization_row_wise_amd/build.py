@@ -15,8 +15,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
-OUT = os.path.join(HERE, "librownorm.so")
-BUILD_DIR = os.path.join(HERE, "_build")
+OUT = os.environ.get("RN_BUILD_OUT", os.path.join(HERE, "librownorm.so"))
+BUILD_DIR = os.environ.get("RN_BUILD_DIR", os.path.join(HERE, "_build"))
 ARCH = os.environ.get("RN_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -27,6 +27,7 @@ FLAGS = [
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    *os.environ.get("RN_EXTRA_FLAGS", "").split(),
 ]
 
 

@@ -16,7 +16,7 @@ namespace rn {
 // so dw / db are bitwise reproducible.  blockIdx.y picks dw (0) or db (1).
 // ------------------------------------------------------------------------------------
 constexpr int CS_THREADS = 256;
-constexpr int CS_C4 = 16;                 // float4 columns per workgroup (64 columns)
+constexpr int CS_C4 = 8;                  // float4 columns per workgroup: one 128-byte line
 constexpr int CS_S = CS_THREADS / CS_C4;  // row slices per workgroup
 
 __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const float* ws, int64_t ldws, int P,
@@ -29,6 +29,7 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const float* ws, int
   const int c = (blockIdx.x * CS_C4 + ci) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < N) {
+#pragma unroll 4
     for (int q = s; q < P; q += CS_S) {
       const float4 v = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(q) * ldws + c);
       acc.x += v.x;
@@ -63,9 +64,16 @@ namespace {
 
 // At most this many partial rows per parameter gradient.  The row-to-workgroup split
 // depends only on (M, N), never on the device, so dw / db are bitwise reproducible.
-constexpr int64_t kMaxPartials = 256;
-// Dynamic LDS budget of the stage-1 team combine.
-constexpr size_t kMaxCombineLds = 60 * 1024;  // + 1 KiB of reduction slots < 64 KiB
+#ifndef RN_MAX_PARTIALS
+#define RN_MAX_PARTIALS 256
+#endif
+constexpr int64_t kMaxPartials = RN_MAX_PARTIALS;
+// Dynamic LDS a backward workgroup may use (gfx950 has 160 KiB per CU; 1 KiB is
+// taken by the static row-reduction slots).
+#ifndef RN_LDS_BUDGET
+#define RN_LDS_BUDGET (156 * 1024)
+#endif
+constexpr size_t kLdsBudget = RN_LDS_BUDGET;
 
 struct Override {
   int v = 0, rows = 0, wg_rows = 0;
@@ -104,13 +112,26 @@ inline bool vec_ok(const void* p, int64_t ld, int64_t M, int eb) {
   return M <= 1 || ((ld * eb) % 16) == 0;
 }
 
-// Smallest compiled V whose team (ceil(N / V) rounded up to whole waves) fits the
-// kernel's workgroup limit, starting from a preferred V.
-inline int pick_v(int64_t N, int preferred) {
+// Elements per thread per row.  Preferred: 64 bytes of each row tensor per lane (32
+// elements of a 16-bit type, 16 of fp32).  Narrow rows use the smallest V that still
+// covers the row with one wave; wide rows move up to a larger V when the team would
+// exceed the kernel's workgroup limit.
+inline int64_t team_of(int64_t N, int v) { return round_up(cdiv(N, v), 64); }
+
+inline int max_wg(int kind, int v, int eb) { return kind == 0 ? fwd_max_wg(v, eb) : bwd_max_wg(v, eb); }
+
+inline int pick_v(int kind, int64_t N, int eb, int requested) {
+  if (requested) {
+    if (team_of(N, requested) <= max_wg(kind, requested, eb)) return requested;
+  }
+  const int pref = eb == 2 ? 32 : 16;
   for (int v : kVs) {
-    if (v < preferred) continue;
-    const int64_t team = round_up(cdiv(N, v), 64);
-    if (team <= max_wg(v)) return v;
+    if (v > pref) break;
+    if (team_of(N, v) == 64) return v;                 // one wave covers the row
+  }
+  for (int v : kVs) {
+    if (v < pref) continue;
+    if (team_of(N, v) <= max_wg(kind, v, eb)) return v;
   }
   return 0;
 }
@@ -123,25 +144,44 @@ struct Shape {
   int64_t grid = 0;
   int P = 0;               // partial rows (backward with grads)
   size_t shmem = 0;
+  int acc = 0;             // backward with grads: accumulators in LDS (1) or VGPRs (0)
 };
 
+// Workgroups a forward (or frozen backward) launch aims for: enough to fill every CU
+// several times over while each workgroup still walks a few rows with prefetch.
+constexpr int64_t kTargetGrid = 2048;
+
 // kind: 0 forward, 1 backward with parameter grads, 2 backward without.
-Shape plan(int kind, int64_t M, int64_t N, int xt) {
+// ngrads: parameter gradients computed (kind 1).
+Shape plan(int kind, int64_t M, int64_t N, int xt, int ngrads = 0) {
   Shape s;
   const Override& o = g_override[kind];
-  // Default elements per thread: forward 16, backward 8 (the backward holds two
-  // input rows plus fp32 accumulators per element).
-  const int pref = kind == 0 ? 16 : 8;
-  s.v = pick_v(N, o.v ? o.v : pref);
-  if (s.v == 0) s.v = pick_v(N, pref);
-  if (s.v == 0) s.v = pick_v(N, 8);
-  s.team = static_cast<int>(round_up(cdiv(N, s.v), 64));
-  const int wg_cap = max_wg(s.v);
-  // Teams per workgroup: about 256 threads by default.
-  int R = o.rows ? o.rows : std::max(1, 256 / s.team);
-  R = std::max(1, std::min(R, wg_cap / s.team));
+  const int eb = elem_bytes(xt);
+  s.v = pick_v(kind, N, eb, o.v);
+  s.team = static_cast<int>(team_of(N, s.v));
+  const int wg_cap = max_wg(kind, s.v, eb);
+  const int r_cap = wg_cap / s.team;
+  int R;
   if (kind == 1) {
-    while (R > 1 && static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) > kMaxCombineLds) --R;
+    const size_t per_team = static_cast<size_t>(ngrads) * s.v * s.team * sizeof(float);
+    if (per_team <= kLdsBudget) {
+      // accumulators in LDS: as many teams as the workgroup and the LDS allow
+      s.acc = 1;
+      const int r_lds = static_cast<int>(kLdsBudget / per_team);
+      R = o.rows ? o.rows : std::min(r_cap, r_lds);
+      R = std::max(1, std::min({R, r_cap, r_lds}));
+      s.shmem = static_cast<size_t>(R) * per_team;
+    } else {
+      // accumulators in VGPRs; LDS only for the final team combine
+      s.acc = 0;
+      R = o.rows ? o.rows : r_cap;
+      R = std::max(1, std::min(R, r_cap));
+      while (R > 1 && static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) > kLdsBudget) --R;
+      s.shmem = R > 1 ? static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) : 0;
+    }
+  } else {
+    R = o.rows ? o.rows : 1;
+    R = std::max(1, std::min(R, r_cap));
   }
   s.R = R;
   if (kind == 1) {
@@ -151,15 +191,13 @@ Shape plan(int kind, int64_t M, int64_t N, int xt) {
     s.rows_per_wg = std::max<int64_t>(rows, R);
     s.P = static_cast<int>(M > 0 ? cdiv(M, s.rows_per_wg) : 0);
     s.grid = s.P;
-    s.shmem = R > 1 ? static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) : 0;
   } else {
-    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : R;
+    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : round_up(cdiv(M, kTargetGrid), R);
     // keep the grid within the 2^31 workgroup limit for very tall inputs
     rows = std::max<int64_t>(rows, round_up(cdiv(M, int64_t(1) << 30), R));
     s.rows_per_wg = std::max<int64_t>(rows, R);
     s.grid = M > 0 ? cdiv(M, s.rows_per_wg) : 0;
   }
-  (void)xt;
   return s;
 }
 
@@ -203,7 +241,7 @@ int rn_set_launch_override(int kind, int v, int rows, int wg_rows) {
   if (kind < 0 || kind > 2 || v < 0 || rows < 0 || wg_rows < 0) return RN_ERR_SHAPE;
   if (v != 0) {
     bool known = false;
-    for (int k : kVs) known = known || (k == v);
+    for (int k : kVs) known = known || (k == v);  // unusable sizes fall back to automatic
     if (!known) return RN_ERR_SHAPE;
   }
   g_override[kind].v = v;
@@ -310,7 +348,7 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   const bool vec = (N % ve) == 0 && vec_ok(dy, lddy, M, eb) && vec_ok(x, ldx, M, eb) &&
                    vec_ok(dx, lddx, M, eb) && vec_ok(dres, lddr, M, eb) && aligned16(w);
 
-  const Shape s = plan(ngrads > 0 ? 1 : 2, M, N, xt);
+  const Shape s = plan(ngrads > 0 ? 1 : 2, M, N, xt, ngrads);
   BwdArgs a{};
   a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
   a.dx = dx; a.lddx = lddx;
@@ -322,9 +360,12 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
            s.shmem};
   bool ok = false;
   const int dxt = to_dt(xt), dwt = to_dt(wt);
-  if (op == OP_RMS) ok = launch_bwd_rms(dxt, dwt, dw != nullptr, l, a, st);
-  else if (op == OP_LN) ok = launch_bwd_ln(dxt, dwt, dw != nullptr, db != nullptr, l, a, st);
-  else ok = launch_bwd_fadd(dxt, dwt, dw != nullptr, l, a, st);
+  // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it
+  const bool xg = (wt != RN_F32) && (op == OP_LN || offset == 0.0f);
+  const BwdVariant bv{dw != nullptr, db != nullptr, xg, s.acc};
+  if (op == OP_RMS) ok = launch_bwd_rms(dxt, dwt, bv, l, a, st);
+  else if (op == OP_LN) ok = launch_bwd_ln(dxt, dwt, bv, l, a, st);
+  else ok = launch_bwd_fadd(dxt, dwt, bv, l, a, st);
   if (!ok) return RN_ERR_DTYPE;
   if ((e = launched()) != RN_OK) return e;
   if (ngrads == 0) return RN_OK;  // frozen: no partials, no second kernel

@@ -2,14 +2,14 @@
 #include "rn_launch.h"
 
 namespace rn {
-bool launch_bwd_ln(int dx, int dw, bool cdw, bool cdb, const Launch& l, const BwdArgs& a,
+bool launch_bwd_ln(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
                    hipStream_t s) {
 #define RN_PAIR(X, W)                                                                  \
   if (dx == X && dw == W) {                                                            \
-    if (cdw && cdb) return bwd_v<OP_LN, X, W, true, true>(l, a, s);                    \
-    if (cdw) return bwd_v<OP_LN, X, W, true, false>(l, a, s);                          \
-    if (cdb) return bwd_v<OP_LN, X, W, false, true>(l, a, s);                          \
-    return bwd_v<OP_LN, X, W, false, false>(l, a, s);                                  \
+    if (b.cdw && b.cdb) return bwd_flags<OP_LN, X, W, true, true>(b, l, a, s);         \
+    if (b.cdw) return bwd_flags<OP_LN, X, W, true, false>(b, l, a, s);                 \
+    if (b.cdb) return bwd_flags<OP_LN, X, W, false, true>(b, l, a, s);                 \
+    return bwd_flags<OP_LN, X, W, false, false>(b, l, a, s);                           \
   }
   RN_FOR_TYPE_PAIRS(RN_PAIR)
 #undef RN_PAIR

@@ -25,6 +25,22 @@ template <> struct Ty<DT_F16> { using S = uint16_t; static constexpr int B = 2; 
 template <> struct Ty<DT_BF16> { using S = uint16_t; static constexpr int B = 2; };
 
 typedef float f2v __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// Buffer resource over `bytes` bytes at `base` (raw, no stride; gfx9 word 3).  `base`
+// must be uniform across the wave.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// A row index every lane of the wave agrees on, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
@@ -92,43 +108,47 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
     for (int j = 0; j < NW; ++j) w[j] = 0u;
   }
 
-  __device__ __forceinline__ void load(const void* rowp, int t, int T, int N, bool valid) {
-    const typename Ty<DT>::S* row = static_cast<const typename Ty<DT>::S*>(rowp);
+  // Load this thread's elements through a buffer resource covering the row: offsets
+  // at or past the resource's byte count read as zero (row tails, rows past M), so
+  // there is no per-access branch and no 64-bit address arithmetic.
+  __device__ __forceinline__ void load(rsrc_t rs, int t, int T) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      const int c = (l * T + t) * VE;
+      const int off = (l * T + t) * VE * B;
       if constexpr (VEC) {
         static_assert(WPL % 4 == 0, "vector access is a whole number of 16-byte loads");
 #pragma unroll
         for (int q = 0; q < WPL / 4; ++q) {
-          uint4 v = make_uint4(0u, 0u, 0u, 0u);
-          if (valid && c < N) v = *reinterpret_cast<const uint4*>(row + c + q * (16 / B));
+          const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + q * 16, 0, 0);
           w[l * WPL + q * 4 + 0] = v.x;
           w[l * WPL + q * 4 + 1] = v.y;
           w[l * WPL + q * 4 + 2] = v.z;
           w[l * WPL + q * 4 + 3] = v.w;
         }
+      } else if constexpr (B == 2) {
+        w[l] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
       } else {
-        w[l] = (valid && c < N) ? static_cast<uint32_t>(row[c]) : 0u;
+        w[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
       }
     }
   }
 
-  // Store words as they are (used for the rounded residual of the fused add).
-  __device__ __forceinline__ void store_raw(void* rowp, int t, int T, int N, bool valid) const {
-    typename Ty<DT>::S* row = static_cast<typename Ty<DT>::S*>(rowp);
+  // Store the words as they are; stores past the resource's byte count are dropped.
+  __device__ __forceinline__ void store_raw(rsrc_t rs, int t, int T) const {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
-      const int c = (l * T + t) * VE;
-      if (!(valid && c < N)) continue;
+      const int off = (l * T + t) * VE * B;
       if constexpr (VEC) {
 #pragma unroll
-        for (int q = 0; q < WPL / 4; ++q)
-          *reinterpret_cast<uint4*>(row + c + q * (16 / B)) =
-              make_uint4(w[l * WPL + q * 4], w[l * WPL + q * 4 + 1], w[l * WPL + q * 4 + 2],
-                         w[l * WPL + q * 4 + 3]);
+        for (int q = 0; q < WPL / 4; ++q) {
+          const v4u v = {w[l * WPL + q * 4], w[l * WPL + q * 4 + 1], w[l * WPL + q * 4 + 2],
+                         w[l * WPL + q * 4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off + q * 16, 0, 0);
+        }
+      } else if constexpr (B == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[l]), rs, off, 0, 0);
       } else {
-        row[c] = static_cast<typename Ty<DT>::S>(w[l]);
+        __builtin_amdgcn_raw_buffer_store_b32(w[l], rs, off, 0, 0);
       }
     }
   }
@@ -148,14 +168,49 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
   }
 };
 
-// Butterfly sum over the 64 lanes of a wave.  Every lane ends with the same value
-// (a + b == b + a exactly), so no broadcast is needed.
+// Make per-column parameters look modified each row, so their fp64 conversions are
+// redone per row instead of being hoisted out of the row loop (which would pin two
+// VGPRs per element for the whole kernel).
+template <int V> __device__ __forceinline__ void opaque(float (&a)[V]) {
+#pragma unroll
+  for (int i = 0; i < V; ++i) asm volatile("" : "+v"(a[i]));
+}
+
+// fp64 value moved across lanes with a DPP pattern (two 32-bit moves).
+template <int CTRL> __device__ __forceinline__ double dpp_mov(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  // every pattern used reads a lane that exists, so no lane keeps an old value
+  const uint32_t lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b), CTRL, 0xF, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double read_lane(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(b), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(b >> 32), lane);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Sum over the 64 lanes of a wave; every lane ends with the same bits.
+// Inside each row of 16 lanes: swap neighbours (quad_perm [1,0,3,2]), swap pairs
+// ([2,3,0,1]), then rotate by 8 and by 4 lanes.  After the two quad swaps all lanes of
+// quad k hold Q_k; rotating by 8 pairs quad k with quad k^2 (Q_k + Q_{k^2}, the same
+// two operands in both quads, and a + b == b + a exactly); rotating by 4 then adds the
+// other pair, again the same two operands everywhere.  The four row sums are read as
+// scalars and added in one fixed order, so the result is uniform.
 template <int NV> __device__ __forceinline__ void wave_sum(double (&v)[NV]) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0xB1>(v[j]);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] += __shfl_xor(v[j], m, 64);
-  }
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0x4E>(v[j]);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0x128>(v[j]);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0x124>(v[j]);
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+    v[j] = (read_lane(v[j], 0) + read_lane(v[j], 16)) + (read_lane(v[j], 32) + read_lane(v[j], 48));
 }
 
 // Sum over the team's waves.  `red` is a workgroup-shared [2][16][4] buffer used in
@@ -176,10 +231,23 @@ __device__ __forceinline__ void team_sum(double (&v)[NV], int wpr, int wave0,
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     double s = red[parity][wave0][j];
+#pragma unroll 1
     for (int q = 1; q < wpr; ++q) s += red[parity][wave0 + q][j];
     v[j] = s;
   }
   parity ^= 1;
+}
+
+// 1 / sqrt(a) for a > 0: fp32 hardware estimate refined by two Newton steps in fp64
+// (each step squares the relative error: ~2^-22 -> 2^-44 -> below fp64 rounding).
+// Outside the range where the fp32 estimate is meaningful, the exact library path.
+__device__ __forceinline__ double rsqrt_d(double a) {
+  if (!(a > 1e-30 && a < 1e30)) return 1.0 / sqrt(a);
+  double r = static_cast<double>(__builtin_amdgcn_rsqf(static_cast<float>(a)));
+  const double h = 0.5 * a;
+  r = r * fma(-h * r, r, 1.5);
+  r = r * fma(-h * r, r, 1.5);
+  return r;
 }
 
 }  // namespace rn

@@ -1,4 +1,4 @@
-// rn_kernels.h — forward, backward (stage 1) and column-sum (stage 2) kernels.
+// rn_kernels.h — forward and backward (stage 1) kernels.
 //
 // Sources (web pages, by title and section):
 //   [frozen] "perf(norm): skip dW/dB calculation when parameters are frozen (#1067)",
@@ -10,12 +10,19 @@
 //            not pre-added in the 16-bit weight type.
 //
 // Arithmetic policy.  Row sums are accumulated in fp64 (full rate on CDNA4 vector
-// ALUs, and this path is bound by HBM, not by the ALUs).  Every output whose value
-// can cancel (LayerNorm y against the bias; every dx) is formed in fp64 from exact
-// fp64 copies of the inputs and rounded once to the output type through fp32.  The
-// backward recomputes the row statistics from x instead of reading a saved fp32
-// rstd: a rounded rstd would carry a 2^-24 relative error that the cancellation in
-// g - xhat * mean(g * xhat) turns into whole-ulp errors of small dx values.
+// ALUs).  Every output whose value can cancel (LayerNorm y against the bias; every
+// dx) is formed in fp64 from exact fp64 copies of the inputs and rounded once to the
+// output type through fp32.  The backward recomputes the row statistics from x
+// instead of reading a saved fp32 rstd: a rounded rstd would carry a 2^-24 relative
+// error that the cancellation in g - xhat * mean(g * xhat) turns into whole-ulp
+// errors of small dx values.  RMSNorm y (no cancellation) is formed in fp32.
+//
+// Work layout.  A team of T = 64 * W threads owns one row at a time (rn_device.h);
+// a workgroup holds R teams and walks rows_per_wg consecutive rows, R at a time.
+// When a thread's share of a row is at most 64 bytes per tensor, the next row's
+// tensors are loaded into a second register set before the current row is reduced
+// (two rows in flight per team).  Columns past N inside the team's span are loaded
+// as zeros; LayerNorm's shifted sums are corrected for them once per row.
 #pragma once
 #include "rn_device.h"
 
@@ -43,19 +50,48 @@ struct BwdArgs {
   float eps, offset;
 };
 
-// ------------------------------------------------------------------------------------
-// Forward.  One team per row; the workgroup holds R = blockDim / team teams and walks
-// rows_per_wg consecutive rows, R at a time.
-// ------------------------------------------------------------------------------------
-// Largest workgroup a kernel with V elements per thread is compiled for: 16 waves
-// (128 VGPRs per lane) up to V = 16, 12 waves (168 VGPRs) above.
-constexpr int max_wg(int V) { return V <= 16 ? 1024 : 768; }
+// Register-budget policy (build-time tunable for launch-shape studies).
+#ifndef RN_FWD_PF_BYTES
+#define RN_FWD_PF_BYTES 64   // forward: prefetch the next row up to this many bytes per lane
+#endif
+#ifndef RN_BWD_PF_BYTES
+#define RN_BWD_PF_BYTES 0    // backward: none (occupancy hides the latency better)
+#endif
+#ifndef RN_FWD_BIG_WG_BYTES
+#define RN_FWD_BIG_WG_BYTES 32   // forward: 1024-thread workgroups up to this many bytes per lane
+#endif
+#ifndef RN_BWD_BIG_WG_BYTES
+#define RN_BWD_BIG_WG_BYTES 0    // backward: always 512 (its fp64 passes need the VGPRs)
+#endif
 
+// Bytes one thread holds of one row of one tensor.
+constexpr int lane_bytes(int V, int B) { return V * B; }
+// Two rows in flight per team when a thread's share is small enough.
+constexpr bool fwd_prefetch(int V, int B) { return lane_bytes(V, B) <= RN_FWD_PF_BYTES; }
+constexpr bool bwd_prefetch(int V, int B) { return lane_bytes(V, B) <= RN_BWD_PF_BYTES; }
+// Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
+// (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.
+constexpr int fwd_max_wg(int V, int B) { return lane_bytes(V, B) <= RN_FWD_BIG_WG_BYTES ? 1024 : 512; }
+constexpr int bwd_max_wg(int V, int B) { return lane_bytes(V, B) <= RN_BWD_BIG_WG_BYTES ? 1024 : 512; }
+
+// The row's first element (0 for a zero-byte resource).
+template <int DX> __device__ __forceinline__ double first_elem(rsrc_t rs) {
+  uint32_t b;
+  if constexpr (Ty<DX>::B == 2) b = __builtin_amdgcn_raw_buffer_load_b16(rs, 0, 0, 0);
+  else b = __builtin_amdgcn_raw_buffer_load_b32(rs, 0, 0, 0);
+  return static_cast<double>(bits_to_f<DX>(b));
+}
+
+// ------------------------------------------------------------------------------------
+// Forward.
+// ------------------------------------------------------------------------------------
 template <int OP, int DX, int DW, int V, bool VEC>
-__global__ __launch_bounds__(max_wg(V)) void fwd_kernel(FwdArgs p) {
+__global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
+  constexpr bool PF = fwd_prefetch(V, Ty<DX>::B);
   using FX = Frag<DX, V, EVE, VEC>;
   using FW = Frag<DW, V, EVE, VEC>;
+  using SX = typename Ty<DX>::S;
   __shared__ double red[2][16][4];
   int parity = 0;
   const int T = p.team;
@@ -67,18 +103,22 @@ __global__ __launch_bounds__(max_wg(V)) void fwd_kernel(FwdArgs p) {
   const int wave0 = (r * T) >> 6;
   const int N = p.N;
   const double inv_n = 1.0 / N;
+  const double pad = static_cast<double>(T * V - N);  // zero-filled slots of the span
 
-  // Weight (and bias) columns owned by this thread, loaded once per workgroup.
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * Ty<DX>::B;
+  const uint32_t par_bytes = static_cast<uint32_t>(N) * Ty<DW>::B;
+
+  // Parameters of this thread's columns, loaded once per workgroup.
   float wv[V];
-  float bv[V];
+  float bv[OP == OP_LN ? V : 1];
   {
     FW wf;
-    wf.load(p.w, t, T, N, true);
+    wf.load(make_rsrc(p.w, par_bytes), t, T);
 #pragma unroll
     for (int i = 0; i < V; ++i) wv[i] = wf.get(i);
     if constexpr (OP == OP_LN) {
       if (p.b != nullptr) {
-        wf.load(p.b, t, T, N, true);
+        wf.load(make_rsrc(p.b, par_bytes), t, T);
 #pragma unroll
         for (int i = 0; i < V; ++i) bv[i] = wf.get(i);
       } else {
@@ -96,22 +136,38 @@ __global__ __launch_bounds__(max_wg(V)) void fwd_kernel(FwdArgs p) {
   const int64_t row_end = min(row_begin + p.rows_per_wg, p.M);
   const int iters = (p.rows_per_wg + R - 1) / R;
 
-  for (int it = 0; it < iters; ++it) {
-    const int64_t row = row_begin + static_cast<int64_t>(it) * R + r;
-    const bool valid = row < row_end;
-    FX xf;
-    xf.load(static_cast<const typename Ty<DX>::S*>(p.x) + row * p.ldx, t, T, N, valid);
+  struct In {
+    FX x;
+    FX res;
+    double k;
+  };
+  // rows are uniform per wave (teams are whole waves); rows past the workgroup's
+  // share get zero-byte resources: their loads read zeros and their stores vanish
+  auto row_of = [&](int it) { return uniform(row_begin + static_cast<int64_t>(it) * R + r); };
+  auto rsrc = [&](const void* base, int64_t ld, int64_t row) {
+    return make_rsrc(static_cast<const SX*>(base) + row * ld, row < row_end ? row_bytes : 0u);
+  };
+  auto load = [&](In& in, int it) {
+    const int64_t row = row_of(it);
+    const rsrc_t rx = rsrc(p.x, p.ldx, row);
+    in.x.load(rx, t, T);
+    if constexpr (OP == OP_FADD) in.res.load(rsrc(p.res, p.ldr, row), t, T);
+    if constexpr (OP == OP_LN) in.k = first_elem<DX>(rx);
+  };
 
+  auto process = [&](In& in, int it) {
+    const int64_t row = row_of(it);
+    const bool valid = row < row_end;
+    opaque<V>(wv);
+    if constexpr (OP == OP_LN) opaque<V>(bv);
+    FX& xf = in.x;
     if constexpr (OP == OP_FADD) {
-      FX rf;
-      rf.load(static_cast<const typename Ty<DX>::S*>(p.res) + row * p.ldr, t, T, N, valid);
       float s[V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) s[i] = xf.get(i) + rf.get(i);
+      for (int i = 0; i < V; ++i) s[i] = xf.get(i) + in.res.get(i);
       xf.pack(s);  // residual_out = round(x + residual); the norm works on this value
-      xf.store_raw(static_cast<typename Ty<DX>::S*>(p.ro) + row * p.ldro, t, T, N, valid);
+      xf.store_raw(rsrc(p.ro, p.ldro, row), t, T);
     }
-
     float o[V];
     if constexpr (OP == OP_RMS || OP == OP_FADD) {
       double acc[1] = {0.0};
@@ -121,65 +177,139 @@ __global__ __launch_bounds__(max_wg(V)) void fwd_kernel(FwdArgs p) {
         acc[0] = fma(v, v, acc[0]);
       }
       team_sum<1>(acc, wpr, wave0, red, parity);
-      const double rstd = 1.0 / sqrt(acc[0] * inv_n + static_cast<double>(p.eps));
+      xf.opaque();
+      const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
       const float rs = static_cast<float>(rstd);
 #pragma unroll
       for (int i = 0; i < V; ++i) o[i] = (xf.get(i) * rs) * wv[i];
       if (valid && t == 0 && p.rstd != nullptr) p.rstd[row] = rs;
-    } else {  // LayerNorm: one pass of shifted sums (shift = the row's first element)
-      const typename Ty<DX>::S* xrow = static_cast<const typename Ty<DX>::S*>(p.x) + row * p.ldx;
-      const double K = valid ? static_cast<double>(bits_to_f<DX>(xrow[0])) : 0.0;
-      double d[V];
+    } else {  // LayerNorm: shifted sums d = x - K with K the row's first element
+      const double K = in.k;
       double acc[2] = {0.0, 0.0};
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        const bool in = FX::inb(i / FX::VE, t, T, N);
-        d[i] = in ? static_cast<double>(xf.get(i)) - K : 0.0;
-        acc[0] += d[i];
-        acc[1] = fma(d[i], d[i], acc[1]);
+        const double d = static_cast<double>(xf.get(i)) - K;
+        acc[0] += d;
+        acc[1] = fma(d, d, acc[1]);
       }
       team_sum<2>(acc, wpr, wave0, red, parity);
+      xf.opaque();
+      acc[0] = fma(pad, K, acc[0]);          // the zero-filled slots added -K each
+      acc[1] = fma(-pad * K, K, acc[1]);     // ... and K^2 each to the squares
       const double delta = acc[0] * inv_n;
       const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
-      const double rstd = 1.0 / sqrt(var + static_cast<double>(p.eps));
+      const double rstd = rsqrt_d(var + static_cast<double>(p.eps));
+      const double mean = K + delta;
 #pragma unroll
-      for (int i = 0; i < V; ++i)
-        o[i] = static_cast<float>(fma((d[i] - delta) * rstd, static_cast<double>(wv[i]),
-                                      static_cast<double>(bv[i])));
+      for (int i = 0; i < V; ++i) {
+        const double e = static_cast<double>(xf.get(i)) - mean;
+        o[i] = static_cast<float>(
+            fma(e * rstd, static_cast<double>(wv[i]), static_cast<double>(bv[i])));
+      }
       if (valid && t == 0) {
         if (p.rstd != nullptr) p.rstd[row] = static_cast<float>(rstd);
-        if (p.mean != nullptr) p.mean[row] = static_cast<float>(K + delta);
+        if (p.mean != nullptr) p.mean[row] = static_cast<float>(mean);
       }
     }
     FX yf;
     yf.pack(o);
-    yf.store_raw(static_cast<typename Ty<DX>::S*>(p.y) + row * p.ldy, t, T, N, valid);
+    yf.store_raw(rsrc(p.y, p.ldy, row), t, T);
+  };
+
+  if constexpr (PF) {
+    In a, b;
+    load(a, 0);
+    for (int it = 0; it < iters; it += 2) {
+      if (it + 1 < iters) load(b, it + 1);
+      process(a, it);
+      if (it + 1 >= iters) break;
+      if (it + 2 < iters) load(a, it + 2);
+      process(b, it + 1);
+    }
+  } else {
+    In a;
+    for (int it = 0; it < iters; ++it) {
+      load(a, it);
+      process(a, it);
+    }
   }
 }
 
-// ------------------------------------------------------------------------------------
-// Backward, stage 1: dx for every row, plus (CDW / CDB) per-thread fp32 accumulators of
-// dw / db over the workgroup's rows, combined across the workgroup's teams in LDS and
-// written as one partial row per workgroup.  With CDW = CDB = false none of that code
-// exists in the kernel ([frozen], Key Changes).
-// ------------------------------------------------------------------------------------
-// Add the R teams' per-thread accumulators in LDS, in team order, and let team 0
-// write the workgroup's partial row.  LDS layout [team-1][element][thread] keeps the
-// 64 lanes of a wave on 64 consecutive words (no bank conflicts).
-template <int V, bool VEC, int EVE, int DX>
-__device__ __forceinline__ void combine_store(float (&acc)[V], float* dst, float* part, int r, int R,
-                                              int t, int T, int N) {
-  using FX = Frag<DX, V, EVE, VEC>;
-  if (R > 1) {
-    if (r > 0) {
+// Parameter-gradient accumulators of one thread: V fp32 partial sums over the rows a
+// team has processed, for the thread's V columns.  Two homes:
+//   ACC = 0: registers (V VGPRs per gradient).
+//   ACC = 1: the workgroup's LDS, one private row of T*V floats per team and gradient
+//            (layout [group of 4 elements][thread][4]: every access is a conflict-free
+//            16-byte ds_read/ds_write).  Frees the VGPRs for more waves per SIMD.
+template <int V, int ACC> struct Acc {
+  static_assert(V % 4 == 0, "accumulators are kept in groups of four");
+  float reg[ACC == 0 ? V : 1];
+  float* lds;  // this thread's base: team row + 4 * t
+  int T;
+
+  __device__ __forceinline__ void init(float* team_row, int t, int T_) {
+    T = T_;
+    if constexpr (ACC == 0) {
 #pragma unroll
-      for (int i = 0; i < V; ++i) part[((r - 1) * V + i) * T + t] = acc[i];
+      for (int i = 0; i < V; ++i) reg[i] = 0.0f;
+    } else {
+      lds = team_row + 4 * t;
+#pragma unroll
+      for (int j = 0; j < V / 4; ++j)
+        *reinterpret_cast<float4*>(lds + 4 * j * T) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    __syncthreads();
-    if (r == 0) {
-      for (int q = 1; q < R; ++q) {
+  }
+  // acc[4j .. 4j+3] += a[k] * b[k], one fused multiply-add each
+  __device__ __forceinline__ void add4(int j, const float (&a)[4], const float (&b)[4]) {
+    if constexpr (ACC == 0) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += part[((q - 1) * V + i) * T + t];
+      for (int k = 0; k < 4; ++k) reg[4 * j + k] = fmaf(a[k], b[k], reg[4 * j + k]);
+    } else {
+      float4* p = reinterpret_cast<float4*>(lds + 4 * j * T);
+      float4 v = *p;
+      v.x = fmaf(a[0], b[0], v.x);
+      v.y = fmaf(a[1], b[1], v.y);
+      v.z = fmaf(a[2], b[2], v.z);
+      v.w = fmaf(a[3], b[3], v.w);
+      *p = v;
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    if constexpr (ACC == 0) return reg[i];
+    else return lds[4 * (i / 4) * T + (i % 4)];
+  }
+};
+
+// Combine the R teams' accumulators, in team order, and let team 0 write the
+// workgroup's partial row `dst` (columns past N are not written).
+template <int V, bool VEC, int EVE, int DX, int ACC>
+__device__ __forceinline__ void combine_store(Acc<V, ACC>& acc, float* dst, float* part, int r,
+                                              int R, int t, int T, int N, int team_stride) {
+  using FX = Frag<DX, V, EVE, VEC>;
+  float tot[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) tot[i] = acc.get(i);
+  if (R > 1) {
+    if constexpr (ACC == 0) {
+      if (r > 0) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) part[((r - 1) * V + i) * T + t] = tot[i];
+      }
+      __syncthreads();
+      if (r == 0) {
+        for (int q = 1; q < R; ++q) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) tot[i] += part[((q - 1) * V + i) * T + t];
+        }
+      }
+    } else {
+      __syncthreads();  // every team's LDS row is complete
+      if (r == 0) {
+        for (int q = 1; q < R; ++q) {
+          const float* o = acc.lds + static_cast<int64_t>(q) * team_stride;
+#pragma unroll
+          for (int i = 0; i < V; ++i) tot[i] += o[4 * (i / 4) * T + (i % 4)];
+        }
       }
     }
   }
@@ -187,17 +317,30 @@ __device__ __forceinline__ void combine_store(float (&acc)[V], float* dst, float
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const int c = FX::col(i, t, T);
-      if (c < N) dst[c] = acc[i];
+      if (c < N) dst[c] = tot[i];
     }
   }
 }
 
-template <int OP, int DX, int DW, int V, bool VEC, bool CDW, bool CDB>
-__global__ __launch_bounds__(max_wg(V)) void bwd_kernel(BwdArgs p) {
+// ------------------------------------------------------------------------------------
+// Backward, stage 1: dx for every row, plus (CDW / CDB) per-thread fp32 accumulators of
+// dw / db over the workgroup's rows, combined across the workgroup's teams and written
+// as one partial row per workgroup.  With CDW = CDB = false none of that code exists in
+// the kernel ([frozen], Key Changes).  dx does not depend on CDW, CDB or ACC.
+// XG: the weight is a 16-bit type and no offset is added, so g = dy * w is exact as an
+// fp32 product (at most 11 + 11 significant bits; exact unless it underflows fp32).
+// ------------------------------------------------------------------------------------
+template <int OP, int DX, int DW, int V, bool VEC, bool CDW, bool CDB, bool XG, int ACC>
+__global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
+  constexpr bool PF = bwd_prefetch(V, Ty<DX>::B);
+  constexpr int NG = (CDW ? 1 : 0) + (CDB ? 1 : 0);
   using FX = Frag<DX, V, EVE, VEC>;
   using FW = Frag<DW, V, EVE, VEC>;
+  using SX = typename Ty<DX>::S;
   static_assert(!(CDB && OP != OP_LN), "only LayerNorm has a bias");
+  static_assert(!(XG && Ty<DW>::B != 2), "exact fp32 products need a 16-bit weight");
+  static_assert(NG > 0 || ACC == 0, "accumulators only exist with parameter gradients");
   __shared__ double red[2][16][4];
   extern __shared__ float part[];
   int parity = 0;
@@ -210,80 +353,110 @@ __global__ __launch_bounds__(max_wg(V)) void bwd_kernel(BwdArgs p) {
   const int wave0 = (r * T) >> 6;
   const int N = p.N;
   const double inv_n = 1.0 / N;
+  const double pad = static_cast<double>(T * V - N);
   const double off = (OP == OP_LN) ? 0.0 : static_cast<double>(p.offset);
 
+  const uint32_t row_bytes = static_cast<uint32_t>(N) * Ty<DX>::B;
   float wv[V];
   {
     FW wf;
-    wf.load(p.w, t, T, N, true);
+    wf.load(make_rsrc(p.w, static_cast<uint32_t>(N) * Ty<DW>::B), t, T);
 #pragma unroll
     for (int i = 0; i < V; ++i) wv[i] = wf.get(i);
   }
-  float dwacc[CDW ? V : 1];
-  float dbacc[CDB ? V : 1];
-#pragma unroll
-  for (int i = 0; i < (CDW ? V : 1); ++i) dwacc[i] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < (CDB ? V : 1); ++i) dbacc[i] = 0.0f;
+  // LDS accumulator rows: [team][gradient][T * V]
+  const int team_stride = NG * T * V;
+  Acc<V, ACC> accw, accb;
+  if constexpr (CDW) accw.init(part + r * team_stride, t, T);
+  if constexpr (CDB) accb.init(part + r * team_stride + (CDW ? T * V : 0), t, T);
 
   const int64_t row_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
   const int64_t row_end = min(row_begin + p.rows_per_wg, p.M);
   const int iters = (p.rows_per_wg + R - 1) / R;
 
-  for (int it = 0; it < iters; ++it) {
-    const int64_t row = row_begin + static_cast<int64_t>(it) * R + r;
-    const bool valid = row < row_end;
-    FX gf, xf;
-    gf.load(static_cast<const typename Ty<DX>::S*>(p.dy) + row * p.lddy, t, T, N, valid);
-    xf.load(static_cast<const typename Ty<DX>::S*>(p.x) + row * p.ldx, t, T, N, valid);
-    float o[V];
+  // g = dy * (w + offset) in fp64 (the offset sum formed exactly), or the exact fp32
+  // product when XG.
+  auto gval = [&](float dys, int i) -> double {
+    if constexpr (XG) return static_cast<double>(dys * wv[i]);
+    else if constexpr (OP == OP_LN) return static_cast<double>(dys) * static_cast<double>(wv[i]);
+    else {
+      const double dyd = static_cast<double>(dys);
+      return fma(dyd, static_cast<double>(wv[i]), dyd * off);
+    }
+  };
 
+  struct In {
+    FX g;   // dy
+    FX x;   // x or residual_out
+    FX d;   // fused add: dres_out
+    double k;
+  };
+  auto row_of = [&](int it) { return uniform(row_begin + static_cast<int64_t>(it) * R + r); };
+  auto rsrc = [&](const void* base, int64_t ld, int64_t row) {
+    return make_rsrc(static_cast<const SX*>(base) + row * ld, row < row_end ? row_bytes : 0u);
+  };
+  auto load = [&](In& in, int it) {
+    const int64_t row = row_of(it);
+    const rsrc_t rx = rsrc(p.x, p.ldx, row);
+    in.g.load(rsrc(p.dy, p.lddy, row), t, T);
+    in.x.load(rx, t, T);
+    if constexpr (OP == OP_FADD) {
+      if (p.dres != nullptr)
+        in.d.load(rsrc(p.dres, p.lddr, row), t, T);
+      else
+        in.d.zero();
+    }
+    if constexpr (OP == OP_LN) in.k = first_elem<DX>(rx);
+  };
+
+  auto process = [&](In& in, int it) {
+    const int64_t row = row_of(it);
+    const bool valid = row < row_end;
+    opaque<V>(wv);
+    FX& gf = in.g;
+    FX& xf = in.x;
+    float o[V];
     if constexpr (OP == OP_RMS || OP == OP_FADD) {
-      FX df;
-      if constexpr (OP == OP_FADD) {
-        if (p.dres != nullptr)
-          df.load(static_cast<const typename Ty<DX>::S*>(p.dres) + row * p.lddr, t, T, N, valid);
-        else
-          df.zero();
-      }
-      double acc[2] = {0.0, 0.0};  // sum x^2, sum g*x with g = dy * (w + offset)
+      double acc[2] = {0.0, 0.0};  // sum x^2, sum g*x
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const double xd = static_cast<double>(xf.get(i));
-        const double gd = static_cast<double>(gf.get(i)) * (static_cast<double>(wv[i]) + off);
+        const double gd = gval(gf.get(i), i);
         acc[0] = fma(xd, xd, acc[0]);
         acc[1] = fma(gd, xd, acc[1]);
       }
       team_sum<2>(acc, wpr, wave0, red, parity);
       xf.opaque();
       gf.opaque();
-      const double rstd = 1.0 / sqrt(acc[0] * inv_n + static_cast<double>(p.eps));
-      // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * (g - x * k), k = rstd^2 * mean(g * x)
-      const double k = rstd * rstd * (acc[1] * inv_n);
+      const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+      // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
+      const double c = rstd * rstd * rstd * (acc[1] * inv_n);
+      // rows past the share read zeros; a zero scale keeps them out of dw even when
+      // rstd is infinite (eps = 0)
+      const float rs = valid ? static_cast<float>(rstd) : 0.0f;
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const double xd = static_cast<double>(xf.get(i));
-        const double gd = static_cast<double>(gf.get(i)) * (static_cast<double>(wv[i]) + off);
-        double dxd = fma(-xd, k, gd) * rstd;
-        if constexpr (OP == OP_FADD) dxd += static_cast<double>(df.get(i));
-        o[i] = static_cast<float>(dxd);
-      }
-      if constexpr (CDW) {
-        if (valid) {
-          const float rs = static_cast<float>(rstd);
+      for (int j = 0; j < V / 4; ++j) {
+        float dyv[4], xh[4];
 #pragma unroll
-          for (int i = 0; i < V; ++i) dwacc[i] = fmaf(gf.get(i), xf.get(i) * rs, dwacc[i]);
+        for (int k = 0; k < 4; ++k) {
+          const int i = 4 * j + k;
+          const float xs = xf.get(i);
+          const float dys = gf.get(i);
+          double dxd = fma(-static_cast<double>(xs), c, gval(dys, i) * rstd);
+          if constexpr (OP == OP_FADD) dxd += static_cast<double>(in.d.get(i));
+          o[i] = static_cast<float>(dxd);
+          dyv[k] = dys;
+          xh[k] = xs * rs;
         }
+        if constexpr (CDW) accw.add4(j, dyv, xh);
       }
     } else {  // LayerNorm
-      const typename Ty<DX>::S* xrow = static_cast<const typename Ty<DX>::S*>(p.x) + row * p.ldx;
-      const double K = valid ? static_cast<double>(bits_to_f<DX>(xrow[0])) : 0.0;
+      const double K = in.k;
       double acc[4] = {0.0, 0.0, 0.0, 0.0};  // sum d, sum d^2, sum g, sum g*d; d = x - K
 #pragma unroll
       for (int i = 0; i < V; ++i) {
-        const bool in = FX::inb(i / FX::VE, t, T, N);
-        const double d = in ? static_cast<double>(xf.get(i)) - K : 0.0;
-        const double g = static_cast<double>(gf.get(i)) * static_cast<double>(wv[i]);
+        const double d = static_cast<double>(xf.get(i)) - K;
+        const double g = gval(gf.get(i), i);
         acc[0] += d;
         acc[1] = fma(d, d, acc[1]);
         acc[2] += g;
@@ -292,46 +465,69 @@ __global__ __launch_bounds__(max_wg(V)) void bwd_kernel(BwdArgs p) {
       team_sum<4>(acc, wpr, wave0, red, parity);
       xf.opaque();
       gf.opaque();
-      const double delta = acc[0] * inv_n;                 // mean - K
+      acc[0] = fma(pad, K, acc[0]);          // zero-filled slots: d = -K, g = 0
+      acc[1] = fma(-pad * K, K, acc[1]);
+      const double delta = acc[0] * inv_n;   // mean - K
       const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
-      const double rstd = 1.0 / sqrt(var + static_cast<double>(p.eps));
+      const double rstd = rsqrt_d(var + static_cast<double>(p.eps));
+      const double mean = K + delta;
       const double mg = acc[2] * inv_n;                    // mean(g)
       const double mgd = acc[3] * inv_n - delta * mg;      // mean(g * (x - mean))
-      const double c2 = mgd * rstd * rstd;             // xhat * mean(g*xhat) = (x-mean) * c2
+      // dx = rstd * (g - mean(g) - (x - mean) * rstd^2 * mean(g * (x - mean)))
+      const double c2 = mgd * rstd * rstd * rstd;
+      const double nmg = -mg * rstd;
+      const float rs = valid ? static_cast<float>(rstd) : 0.0f;
+      const float nmr = valid ? static_cast<float>(-mean * rstd) : 0.0f;
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        const bool in = FX::inb(i / FX::VE, t, T, N);
-        const double e = (in ? static_cast<double>(xf.get(i)) - K : 0.0) - delta;
-        const double g = static_cast<double>(gf.get(i)) * static_cast<double>(wv[i]);
-        o[i] = static_cast<float>(fma(-e, c2, g - mg) * rstd);
-      }
-      if constexpr (CDW || CDB) {
-        if (valid) {
+      for (int j = 0; j < V / 4; ++j) {
+        float dyv[4], xh[4];
+        const float one[4] = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
-          for (int i = 0; i < V; ++i) {
-            if constexpr (CDW) {
-              const bool in = FX::inb(i / FX::VE, t, T, N);
-              const double e = (in ? static_cast<double>(xf.get(i)) - K : 0.0) - delta;
-              dwacc[i] = fmaf(gf.get(i), static_cast<float>(e * rstd), dwacc[i]);
-            }
-            if constexpr (CDB) dbacc[i] += gf.get(i);
-          }
+        for (int k = 0; k < 4; ++k) {
+          const int i = 4 * j + k;
+          const float xs = xf.get(i);
+          const float dys = gf.get(i);
+          const double e = static_cast<double>(xs) - mean;
+          o[i] = static_cast<float>(fma(-e, c2, fma(gval(dys, i), rstd, nmg)));
+          dyv[k] = dys;
+          xh[k] = fmaf(xs, rs, nmr);
         }
+        if constexpr (CDW) accw.add4(j, dyv, xh);
+        if constexpr (CDB) accb.add4(j, dyv, one);
       }
     }
     FX of;
     of.pack(o);
-    of.store_raw(static_cast<typename Ty<DX>::S*>(p.dx) + row * p.lddx, t, T, N, valid);
+    of.store_raw(rsrc(p.dx, p.lddx, row), t, T);
+  };
+
+  if constexpr (PF) {
+    In a, b;
+    load(a, 0);
+    for (int it = 0; it < iters; it += 2) {
+      if (it + 1 < iters) load(b, it + 1);
+      process(a, it);
+      if (it + 1 >= iters) break;
+      if (it + 2 < iters) load(a, it + 2);
+      process(b, it + 1);
+    }
+  } else {
+    In a;
+    for (int it = 0; it < iters; ++it) {
+      load(a, it);
+      process(a, it);
+    }
   }
 
   if constexpr (CDW) {
-    combine_store<V, VEC, EVE, DX>(dwacc, p.ws + static_cast<int64_t>(blockIdx.x) * p.ldws, part,
-                                  r, R, t, T, N);
+    combine_store<V, VEC, EVE, DX, ACC>(accw, p.ws + static_cast<int64_t>(blockIdx.x) * p.ldws,
+                                        part, r, R, t, T, N, team_stride);
   }
   if constexpr (CDB) {
-    if constexpr (CDW) __syncthreads();  // LDS is reused after the dw pass
-    combine_store<V, VEC, EVE, DX>(
-        dbacc, p.ws + (static_cast<int64_t>(CDW ? p.P : 0) + blockIdx.x) * p.ldws, part, r, R, t, T, N);
+    if constexpr (CDW && ACC == 0) __syncthreads();  // the register path reuses `part`
+    combine_store<V, VEC, EVE, DX, ACC>(
+        accb, p.ws + (static_cast<int64_t>(CDW ? p.P : 0) + blockIdx.x) * p.ldws, part, r, R, t, T,
+        N, team_stride);
   }
 }
 

@@ -6,7 +6,7 @@
 namespace rn {
 
 // Elements per thread per row that are compiled (for every type and both access modes).
-constexpr int kVs[] = {8, 16, 24, 32};
+constexpr int kVs[] = {8, 16, 32, 48};
 
 struct Launch {
   int v;          // elements per thread per row (one of kVs)
@@ -19,10 +19,18 @@ struct Launch {
 bool launch_fwd_rms(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
 bool launch_fwd_ln(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
 bool launch_fwd_fadd(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
-bool launch_bwd_rms(int dx, int dw, bool cdw, const Launch& l, const BwdArgs& a, hipStream_t s);
-bool launch_bwd_ln(int dx, int dw, bool cdw, bool cdb, const Launch& l, const BwdArgs& a,
+// Backward variants: xg = exact fp32 product g = dy * w (16-bit weight, no offset);
+// acc = 1 keeps the dw / db accumulators in LDS, 0 in registers (V >= 32 only).
+struct BwdVariant {
+  bool cdw, cdb, xg;
+  int acc;
+};
+bool launch_bwd_rms(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
+                    hipStream_t s);
+bool launch_bwd_ln(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
                    hipStream_t s);
-bool launch_bwd_fadd(int dx, int dw, bool cdw, const Launch& l, const BwdArgs& a, hipStream_t s);
+bool launch_bwd_fadd(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
+                     hipStream_t s);
 
 // Type pairs that are compiled: (x type, weight type).
 #define RN_FOR_TYPE_PAIRS(X)                                                    \
@@ -36,19 +44,56 @@ inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
     if (l.vec) fwd_kernel<OP, DX, DW, V, true><<<l.grid, l.block, l.shmem, s>>>(a);  \
     else fwd_kernel<OP, DX, DW, V, false><<<l.grid, l.block, l.shmem, s>>>(a);       \
     return true;
-  switch (l.v) { RN_CASE(8) RN_CASE(16) RN_CASE(24) RN_CASE(32) default: return false; }
+  switch (l.v) { RN_CASE(8) RN_CASE(16) RN_CASE(32) RN_CASE(48) default: return false; }
 #undef RN_CASE
 }
 
-template <int OP, int DX, int DW, bool CDW, bool CDB>
-inline bool bwd_v(const Launch& l, const BwdArgs& a, hipStream_t s) {
-#define RN_CASE(V)                                                                            \
-  case V:                                                                                     \
-    if (l.vec) bwd_kernel<OP, DX, DW, V, true, CDW, CDB><<<l.grid, l.block, l.shmem, s>>>(a); \
-    else bwd_kernel<OP, DX, DW, V, false, CDW, CDB><<<l.grid, l.block, l.shmem, s>>>(a);      \
+template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, int ACC, int V>
+inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
+  if constexpr (ACC == 0 && (CDW || CDB) && V < 32) {
+    return false;  // narrow rows always fit their accumulators in LDS
+  } else {
+    auto k = l.vec ? bwd_kernel<OP, DX, DW, V, true, CDW, CDB, XG, ACC>
+                   : bwd_kernel<OP, DX, DW, V, false, CDW, CDB, XG, ACC>;
+    if (l.shmem > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(l.shmem)) != hipSuccess)
+      return false;
+    k<<<l.grid, l.block, l.shmem, s>>>(a);
     return true;
-  switch (l.v) { RN_CASE(8) RN_CASE(16) RN_CASE(24) RN_CASE(32) default: return false; }
-#undef RN_CASE
+  }
+}
+
+template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, int ACC>
+inline bool bwd_v(const Launch& l, const BwdArgs& a, hipStream_t s) {
+  switch (l.v) {
+    case 8: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 8>(l, a, s);
+    case 16: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 16>(l, a, s);
+    case 32: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 32>(l, a, s);
+    case 48: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 48>(l, a, s);
+    default: return false;
+  }
+}
+
+// Dispatch over the gradient flags, the exact-product path and the accumulator home.
+template <int OP, int DX, int DW, bool CDW, bool CDB>
+inline bool bwd_flags(const BwdVariant& b, const Launch& l, const BwdArgs& a, hipStream_t s) {
+  constexpr bool can_xg = Ty<DW>::B == 2;
+  if constexpr (!CDW && !CDB) {
+    if constexpr (can_xg) {
+      if (b.xg) return bwd_v<OP, DX, DW, false, false, true, 0>(l, a, s);
+    }
+    return bwd_v<OP, DX, DW, false, false, false, 0>(l, a, s);
+  } else {
+    if constexpr (can_xg) {
+      if (b.xg)
+        return b.acc ? bwd_v<OP, DX, DW, CDW, CDB, true, 1>(l, a, s)
+                     : bwd_v<OP, DX, DW, CDW, CDB, true, 0>(l, a, s);
+    }
+    return b.acc ? bwd_v<OP, DX, DW, CDW, CDB, false, 1>(l, a, s)
+                 : bwd_v<OP, DX, DW, CDW, CDB, false, 0>(l, a, s);
+  }
 }
 
 }  // namespace rn
