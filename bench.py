@@ -34,6 +34,33 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    """Hash of the kernel sources: counter summaries are valid only for this hash."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "normalization_row_wise_amd", "csrc")
+    for f in sorted(os.listdir(csrc)) + ["../../../include/rownorm.h"]:
+        path = os.path.normpath(os.path.join(csrc, f))
+        if os.path.isfile(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel_key: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel's readings), or None when
+    the summary is missing or was taken from other kernel sources."""
+    path = os.path.join(PROFILES, f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != source_hash() or kernel_key not in d.get("kernels", {}):
+        return None
+    k = d["kernels"][kernel_key]
+    return int(round((k["fetch_kib"] * d["fetch_scale"] + k["write_kib"] * d["write_scale"]) * 1024))
 
 
 def alg_bytes(wl: workloads.Workload, trainable: bool) -> dict:
@@ -159,33 +186,34 @@ def time_steps(sets, K, W, use_graph, torch):
 
 
 def event_times(sets, n, rn, torch):
-    """Per-kernel device time (us) from HIP events on the launch stream: forward,
-    backward stage 1 (dx + partials) and the whole backward call.  A spin kernel
-    holds the GPU while the host enqueues every step, so the GPU then runs them back
-    to back and the events time kernels, not host launch gaps."""
+    """Per-kernel device times (us) from HIP events on the launch stream.
+
+    The forward kernel and the first backward kernel (dx + partial rows) are launched
+    through hipExtLaunchKernel with a start/stop event pair, so each pair brackets
+    exactly one kernel (the dispatch records both).  The whole backward call (both
+    kernels) is bracketed by ordinary events.  A spin kernel holds the GPU while the
+    host enqueues every step, so the GPU then runs them back to back."""
     st = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
-    trainable = sets.sets[0]["dw"] is not None or sets.sets[0]["db"] is not None
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[mk() for _ in range(6)] for _ in range(n)]
+    for e in (x for row in ev for x in row):
+        e.record(st)                      # materialise the event handles
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * n)))   # ~ 2 ms + 40 us per step
     for k in range(n):
-        e0, e1, e2, e3 = ev[k]
-        e0.record(st)
+        f0, f1, b0, b1, c0, c1 = ev[k]
+        rn.set_timing_events(0, f0, f1)
         sets.fwd(k % sets.S)
-        e1.record(st)
-        if trainable:
-            e2.record(st)       # materialise the handle, then let the library re-record it
-            rn.set_stage_event(e2)
+        rn.set_timing_events(0, None, None)
+        rn.set_timing_events(1, b0, b1)
+        c0.record(st)
         sets.bwd((k + sets.S // 2) % sets.S)
-        if trainable:
-            rn.set_stage_event(None)
-        else:
-            e2.record(st)
-        e3.record(st)
+        c1.record(st)
+        rn.set_timing_events(1, None, None)
     torch.cuda.synchronize()
     f = [ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(n)]
-    b1 = [ev[k][1].elapsed_time(ev[k][2]) * 1e3 for k in range(n)]
-    b = [ev[k][1].elapsed_time(ev[k][3]) * 1e3 for k in range(n)]
+    b1 = [ev[k][2].elapsed_time(ev[k][3]) * 1e3 for k in range(n)]
+    b = [ev[k][4].elapsed_time(ev[k][5]) * 1e3 for k in range(n)]
     med = lambda a: sorted(a)[len(a) // 2]
     mean = lambda a: sum(a) / len(a)
     return {"fwd_us_median": med(f), "bwd_stage1_us_median": med(b1), "bwd_us_median": med(b),
@@ -242,7 +270,20 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--event-steps", type=int, default=200)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy * 2**20 // 2
+        a = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_mib": args.calibrate_copy}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -275,11 +316,13 @@ def main():
         fsecs, fk = time_steps(fz, args.steps, args.warmup, not args.eager, torch)
         fev = event_times(fz, args.event_steps, rn, torch)
         other = {"frozen_us_per_step": round(fsecs / fk * 1e6, 3),
-                 "frozen_bwd_us_median": round(fev["bwd_us_median"], 3)}
+                 "frozen_bwd_kernel_us": round(fev["bwd_stage1_us_median"], 3)}
         del fz
 
-    stage1_us = ev["bwd_stage1_us_mean"] if trainable else ev["bwd_us_median"]
+    stage1_us = ev["bwd_stage1_us_mean"]
     achieved = ab["bwd_stage1"] / (stage1_us * 1e-6) / 1e9
+    kernel_key = "bwd_stage1_trainable" if trainable else "bwd_frozen"
+    traffic = measured_traffic(wl.name, kernel_key)
     line = {
         "metric": "achieved HBM GB/s (% of peak) & µs/call, bf16 norm fwd+bwd at M×N",
         "value": round(gbs, 2),
@@ -297,15 +340,15 @@ def main():
                    "weight": wl.wt, "trainable_params": trainable,
                    "timing": "eager" if args.eager else "hip graph replay", "buffer_sets": S},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "us_per_call": {"fwd": round(ev["fwd_us_median"], 3),
-                        "bwd_stage1": round(ev["bwd_stage1_us_median"], 3),
-                        "bwd": round(ev["bwd_us_median"], 3),
-                        "fwd_plus_bwd": round(ev["fwd_us_median"] + ev["bwd_us_median"], 3)},
+        "us_per_call": {"fwd_kernel": round(ev["fwd_us_median"], 3),
+                        "bwd_stage1_kernel": round(ev["bwd_stage1_us_median"], 3),
+                        "bwd_call_events": round(ev["bwd_us_median"], 3),
+                        "step_wall": round(ms * 1e3, 3)},
         **other,
         "roofline": {"kernel": "bwd_kernel (stage 1: dx + dW/dB partial rows)" if trainable
-                     else "bwd_kernel (frozen)",
+                     else "bwd_kernel (frozen parameters: dx only)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": ab["bwd_stage1"],
                      "avg_launch_us": round(stage1_us, 3)},
     }

@@ -142,11 +142,13 @@ const char* rn_status_str(int status);
  *   shape that cannot run the problem is ignored.  Returns RN_OK or RN_ERR_SHAPE. */
 int rn_set_launch_override(int kind, int v, int rows, int wg_rows);
 
-/* Instrumentation for timing the two backward stages separately.  While `ev` is not
- * NULL, every backward call that computes parameter gradients records `ev` on its
- * stream between its first kernel (dx and partial rows) and its column-sum kernel.
- * Pass NULL to stop.  Process-wide; not thread-safe.  Always returns RN_OK. */
-int rn_set_stage_event(hipEvent_t ev);
+/* Instrumentation for timing single kernels.  While `start` and `stop` are not NULL,
+ * every launch of the chosen kernel family records its own start and end times into
+ * them (hipExtLaunchKernel events, taken by the dispatch itself): kernel 0 = forward
+ * kernels, 1 = first backward kernel (dx and partial rows).  Pass NULLs to stop.
+ * Process-wide; not thread-safe.  Returns RN_OK, or RN_ERR_SHAPE for another
+ * kernel number. */
+int rn_set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ _SIGS = {
     "rn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "rn_status_str": (ctypes.c_char_p, [_i32]),
     "rn_set_launch_override": (_i32, [_i32, _i32, _i32, _i32]),
-    "rn_set_stage_event": (_i32, [_vp]),
+    "rn_set_timing_events": (_i32, [_i32, _vp, _vp]),
     "rmsnorm_fwd": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _f32, _f32, _i32, _i32, _vp]),
     "rmsnorm_bwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _i64, _i64, _f32,
                            _f32, _i32, _i32, _vp]),
@@ -119,9 +119,12 @@ def set_launch_override(kind: int, v: int = 0, rows: int = 0, wg_rows: int = 0) 
     _check(lib.rn_set_launch_override(kind, v, rows, wg_rows))
 
 
-def set_stage_event(event) -> None:
-    """Record a torch.cuda.Event between the two backward kernels (None to stop)."""
-    _check(lib.rn_set_stage_event(None if event is None else ctypes.c_void_p(event.cuda_event)))
+def set_timing_events(kernel: int, start=None, stop=None) -> None:
+    """Time every launch of one kernel family with two torch.cuda.Events (recorded by
+    the dispatch itself): kernel 0 = forward, 1 = first backward kernel.  The events
+    must have been recorded once (so that they exist).  None, None stops."""
+    h = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
+    _check(lib.rn_set_timing_events(kernel, h(start), h(stop)))
 
 
 def rmsnorm_fwd(x, w, eps: float = 1e-6, offset: float = 0.0, *, y=None, rstd=True, stream=None):
@@ -212,7 +215,7 @@ def fused_add_rmsnorm_bwd(dy, residual_out, w, eps: float = 1e-6, offset: float 
 
 __all__ = [
     "lib", "LIB_PATH", "RowNormError", "workspace_bytes", "set_launch_override",
-    "set_stage_event",
+    "set_timing_events",
     "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
     "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_bwd",
 ]

@@ -79,7 +79,7 @@ struct Override {
   int v = 0, rows = 0, wg_rows = 0;
 };
 Override g_override[3];  // 0: forward, 1: backward with grads, 2: backward without
-hipEvent_t g_stage_event = nullptr;
+hipEvent_t g_timing[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};  // [kernel][start, stop]
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -250,8 +250,10 @@ int rn_set_launch_override(int kind, int v, int rows, int wg_rows) {
   return RN_OK;
 }
 
-int rn_set_stage_event(hipEvent_t ev) {
-  g_stage_event = ev;
+int rn_set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop) {
+  if (kernel < 0 || kernel > 1) return RN_ERR_SHAPE;
+  g_timing[kernel][0] = start;
+  g_timing[kernel][1] = stop;
   return RN_OK;
 }
 
@@ -286,7 +288,7 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
   Launch l{s.v, vec, dim3(static_cast<unsigned>(s.grid)), dim3(static_cast<unsigned>(s.R * s.team)),
-           0};
+           0, g_timing[0][0], g_timing[0][1]};
   bool ok = false;
   const int dx = to_dt(xt), dw = to_dt(wt);
   if (op == OP_RMS) ok = launch_fwd_rms(dx, dw, l, a, st);
@@ -357,7 +359,7 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
   Launch l{s.v, vec, dim3(static_cast<unsigned>(s.grid)), dim3(static_cast<unsigned>(s.R * s.team)),
-           s.shmem};
+           s.shmem, g_timing[1][0], g_timing[1][1]};
   bool ok = false;
   const int dxt = to_dt(xt), dwt = to_dt(wt);
   // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it
@@ -369,7 +371,6 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   if (!ok) return RN_ERR_DTYPE;
   if ((e = launched()) != RN_OK) return e;
   if (ngrads == 0) return RN_OK;  // frozen: no partials, no second kernel
-  if (g_stage_event != nullptr && hipEventRecord(g_stage_event, st) != hipSuccess) return RN_ERR_HIP;
   return colsum(static_cast<const float*>(ws), ldws, s.P, N, dw, db, st);
 }
 

@@ -1,5 +1,6 @@
 // rn_launch.h — internal launch interface between the C ABI and the kernel instances.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include "rn_kernels.h"
 
@@ -13,7 +14,17 @@ struct Launch {
   bool vec;       // 16-byte accesses (else element accesses)
   dim3 grid, block;
   size_t shmem;   // dynamic LDS bytes
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional kernel timing
 };
+
+// Launch through hipExtLaunchKernel when timing events are attached.
+template <typename K, typename A>
+inline void launch_kernel(K k, const Launch& l, hipStream_t s, const A& a) {
+  if (l.ev_start != nullptr && l.ev_stop != nullptr)
+    hipExtLaunchKernelGGL(k, l.grid, l.block, l.shmem, s, l.ev_start, l.ev_stop, 0, a);
+  else
+    k<<<l.grid, l.block, l.shmem, s>>>(a);
+}
 
 // Each returns false when (dx, dw, v) has no compiled instance.
 bool launch_fwd_rms(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
@@ -39,10 +50,10 @@ bool launch_bwd_fadd(int dx, int dw, const BwdVariant& b, const Launch& l, const
 
 template <int OP, int DX, int DW>
 inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
-#define RN_CASE(V)                                                                   \
-  case V:                                                                            \
-    if (l.vec) fwd_kernel<OP, DX, DW, V, true><<<l.grid, l.block, l.shmem, s>>>(a);  \
-    else fwd_kernel<OP, DX, DW, V, false><<<l.grid, l.block, l.shmem, s>>>(a);       \
+#define RN_CASE(V)                                                                       \
+  case V:                                                                                \
+    launch_kernel(l.vec ? fwd_kernel<OP, DX, DW, V, true> : fwd_kernel<OP, DX, DW, V, false>, \
+                  l, s, a);                                                              \
     return true;
   switch (l.v) { RN_CASE(8) RN_CASE(16) RN_CASE(32) RN_CASE(48) default: return false; }
 #undef RN_CASE
@@ -60,7 +71,7 @@ inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(l.shmem)) != hipSuccess)
       return false;
-    k<<<l.grid, l.block, l.shmem, s>>>(a);
+    launch_kernel(k, l, s, a);
     return true;
   }
 }
