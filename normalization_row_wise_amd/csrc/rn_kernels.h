@@ -18,7 +18,10 @@
 // errors of small dx values.  RMSNorm y (no cancellation) is formed in fp32.
 //
 // Work layout.  A team of T = 64 * W threads owns one row at a time (rn_device.h);
-// a workgroup holds R teams and walks rows_per_wg consecutive rows, R at a time.
+// a workgroup holds R teams and makes rows_per_wg / R passes.  Pass `it` of workgroup
+// `b` takes rows (it * grid + b) * R .. + R - 1 (grid-stride): the rows in flight
+// across the chip at any moment form one contiguous window of the tensor, instead of
+// one slice per workgroup scattered over all of it (measured faster at large M).
 // When a thread's share of a row is at most 64 bytes per tensor, the next row's
 // tensors are loaded into a second register set before the current row is reduced
 // (two rows in flight per team).  Columns past N inside the team's span are loaded
@@ -132,8 +135,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
     }
   }
 
-  const int64_t row_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
-  const int64_t row_end = min(row_begin + p.rows_per_wg, p.M);
+  const int64_t row_end = p.M;
   const int iters = (p.rows_per_wg + R - 1) / R;
 
   struct In {
@@ -143,7 +145,9 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
   };
   // rows are uniform per wave (teams are whole waves); rows past the workgroup's
   // share get zero-byte resources: their loads read zeros and their stores vanish
-  auto row_of = [&](int it) { return uniform(row_begin + static_cast<int64_t>(it) * R + r); };
+  auto row_of = [&](int it) {
+    return uniform((static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R + r);
+  };
   auto rsrc = [&](const void* base, int64_t ld, int64_t row) {
     return make_rsrc(static_cast<const SX*>(base) + row * ld, row < row_end ? row_bytes : 0u);
   };
@@ -217,13 +221,16 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
   };
 
   if constexpr (PF) {
+    // The next row's loads are issued unconditionally (past the share they read
+    // zeros): a load issued on one path only makes the wait before the current row's
+    // data a full vmcnt(0), which also waits for the previous row's stores.
     In a, b;
     load(a, 0);
     for (int it = 0; it < iters; it += 2) {
-      if (it + 1 < iters) load(b, it + 1);
+      load(b, it + 1);
       process(a, it);
       if (it + 1 >= iters) break;
-      if (it + 2 < iters) load(a, it + 2);
+      load(a, it + 2);
       process(b, it + 1);
     }
   } else {
@@ -370,8 +377,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   if constexpr (CDW) accw.init(part + r * team_stride, t, T);
   if constexpr (CDB) accb.init(part + r * team_stride + (CDW ? T * V : 0), t, T);
 
-  const int64_t row_begin = static_cast<int64_t>(blockIdx.x) * p.rows_per_wg;
-  const int64_t row_end = min(row_begin + p.rows_per_wg, p.M);
+  const int64_t row_end = p.M;
   const int iters = (p.rows_per_wg + R - 1) / R;
 
   // g = dy * (w + offset) in fp64 (the offset sum formed exactly), or the exact fp32
@@ -391,7 +397,9 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     FX d;   // fused add: dres_out
     double k;
   };
-  auto row_of = [&](int it) { return uniform(row_begin + static_cast<int64_t>(it) * R + r); };
+  auto row_of = [&](int it) {
+    return uniform((static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R + r);
+  };
   auto rsrc = [&](const void* base, int64_t ld, int64_t row) {
     return make_rsrc(static_cast<const SX*>(base) + row * ld, row < row_end ? row_bytes : 0u);
   };
@@ -502,13 +510,16 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   };
 
   if constexpr (PF) {
+    // The next row's loads are issued unconditionally (past the share they read
+    // zeros): a load issued on one path only makes the wait before the current row's
+    // data a full vmcnt(0), which also waits for the previous row's stores.
     In a, b;
     load(a, 0);
     for (int it = 0; it < iters; it += 2) {
-      if (it + 1 < iters) load(b, it + 1);
+      load(b, it + 1);
       process(a, it);
       if (it + 1 >= iters) break;
-      if (it + 2 < iters) load(a, it + 2);
+      load(a, it + 2);
       process(b, it + 1);
     }
   } else {
