@@ -58,8 +58,11 @@ struct BwdArgs {
 #define RN_FWD_PF_BYTES 64   // forward: prefetch the next row up to this many bytes per lane
 #endif
 #ifndef RN_BWD_PF_BYTES
-#define RN_BWD_PF_BYTES 0    // backward: none (occupancy hides the latency better)
+#define RN_BWD_PF_BYTES 64   // backward with parameter gradients: as the forward
 #endif
+#ifndef RN_FROZEN_PF_BYTES
+#define RN_FROZEN_PF_BYTES 0   // backward without: none (its many short-lived workgroups
+#endif                         // hide the latency better)
 #ifndef RN_FWD_BIG_WG_BYTES
 #define RN_FWD_BIG_WG_BYTES 32   // forward: 1024-thread workgroups up to this many bytes per lane
 #endif
@@ -71,7 +74,11 @@ struct BwdArgs {
 constexpr int lane_bytes(int V, int B) { return V * B; }
 // Two rows in flight per team when a thread's share is small enough.
 constexpr bool fwd_prefetch(int V, int B) { return lane_bytes(V, B) <= RN_FWD_PF_BYTES; }
-constexpr bool bwd_prefetch(int V, int B) { return lane_bytes(V, B) <= RN_BWD_PF_BYTES; }
+// `nin` row tensors are read per row (2, or 3 for the fused add's backward): the limit
+// is for two, so a third tensor lowers it in proportion.
+constexpr bool bwd_prefetch(int V, int B, bool grads, int nin) {
+  return lane_bytes(V, B) * nin <= 2 * (grads ? RN_BWD_PF_BYTES : RN_FROZEN_PF_BYTES);
+}
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
 // (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.
 constexpr int fwd_max_wg(int V, int B) { return lane_bytes(V, B) <= RN_FWD_BIG_WG_BYTES ? 1024 : 512; }
@@ -281,42 +288,29 @@ template <int V, int ACC> struct Acc {
       *p = v;
     }
   }
-  __device__ __forceinline__ float get(int i) const {
-    if constexpr (ACC == 0) return reg[i];
-    else return lds[4 * (i / 4) * T + (i % 4)];
-  }
+  __device__ __forceinline__ float get(int i) const { return reg[i]; }  // ACC = 0
 };
 
-// Combine the R teams' accumulators, in team order, and let team 0 write the
-// workgroup's partial row `dst` (columns past N are not written).
-template <int V, bool VEC, int EVE, int DX, int ACC>
-__device__ __forceinline__ void combine_store(Acc<V, ACC>& acc, float* dst, float* part, int r,
-                                              int R, int t, int T, int N, int team_stride) {
+// Register accumulators (ACC = 0): the R teams' sums are added in team order through
+// `part` and team 0 writes the workgroup's partial row `dst` (columns past N are not
+// written).
+template <int V, bool VEC, int EVE, int DX>
+__device__ __forceinline__ void combine_regs(const Acc<V, 0>& acc, float* dst, float* part, int r,
+                                             int R, int t, int T, int N) {
   using FX = Frag<DX, V, EVE, VEC>;
   float tot[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) tot[i] = acc.get(i);
   if (R > 1) {
-    if constexpr (ACC == 0) {
-      if (r > 0) {
+    if (r > 0) {
 #pragma unroll
-        for (int i = 0; i < V; ++i) part[((r - 1) * V + i) * T + t] = tot[i];
-      }
-      __syncthreads();
-      if (r == 0) {
-        for (int q = 1; q < R; ++q) {
+      for (int i = 0; i < V; ++i) part[((r - 1) * V + i) * T + t] = tot[i];
+    }
+    __syncthreads();
+    if (r == 0) {
+      for (int q = 1; q < R; ++q) {
 #pragma unroll
-          for (int i = 0; i < V; ++i) tot[i] += part[((q - 1) * V + i) * T + t];
-        }
-      }
-    } else {
-      __syncthreads();  // every team's LDS row is complete
-      if (r == 0) {
-        for (int q = 1; q < R; ++q) {
-          const float* o = acc.lds + static_cast<int64_t>(q) * team_stride;
-#pragma unroll
-          for (int i = 0; i < V; ++i) tot[i] += o[4 * (i / 4) * T + (i % 4)];
-        }
+        for (int i = 0; i < V; ++i) tot[i] += part[((q - 1) * V + i) * T + t];
       }
     }
   }
@@ -325,6 +319,41 @@ __device__ __forceinline__ void combine_store(Acc<V, ACC>& acc, float* dst, floa
     for (int i = 0; i < V; ++i) {
       const int c = FX::col(i, t, T);
       if (c < N) dst[c] = tot[i];
+    }
+  }
+}
+
+// LDS accumulators (ACC = 1): every team takes part.  Team r handles the groups of four
+// elements j = r, r + R, ...; for each, thread t adds the R teams' float4 in team order
+// (16-byte, conflict-free LDS reads) and writes the four columns of the partial row
+// `dst`.  The sums are the same as adding the teams' rows element by element in team
+// order.  The caller has synchronised the workgroup after the last accumulation.
+template <int V, bool VEC, int EVE, int DX>
+__device__ __forceinline__ void combine_lds(const float* rows, float* dst, int r, int R, int t,
+                                            int T, int N, int team_stride) {
+  using FX = Frag<DX, V, EVE, VEC>;
+  for (int j = r; j < V / 4; j += R) {
+    const float* src = rows + 4 * (j * T + t);
+    float4 a = *reinterpret_cast<const float4*>(src);
+    for (int q = 1; q < R; ++q) {
+      const float4 b = *reinterpret_cast<const float4*>(src + q * team_stride);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    if constexpr (VEC) {
+      // a group lies inside one access of VE >= 4 contiguous columns, and N is a
+      // multiple of VE: the group is wholly inside the row or wholly outside
+      const int c0 = FX::col(4 * j, t, T);
+      if (c0 < N) *reinterpret_cast<float4*>(dst + c0) = a;
+    } else {
+      const float v[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = FX::col(4 * j + k, t, T);
+        if (c < N) dst[c] = v[k];
+      }
     }
   }
 }
@@ -340,8 +369,8 @@ __device__ __forceinline__ void combine_store(Acc<V, ACC>& acc, float* dst, floa
 template <int OP, int DX, int DW, int V, bool VEC, bool CDW, bool CDB, bool XG, int ACC>
 __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
-  constexpr bool PF = bwd_prefetch(V, Ty<DX>::B);
   constexpr int NG = (CDW ? 1 : 0) + (CDB ? 1 : 0);
+  constexpr bool PF = bwd_prefetch(V, Ty<DX>::B, NG > 0, OP == OP_FADD ? 3 : 2);
   using FX = Frag<DX, V, EVE, VEC>;
   using FW = Frag<DW, V, EVE, VEC>;
   using SX = typename Ty<DX>::S;
@@ -530,15 +559,19 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     }
   }
 
-  if constexpr (CDW) {
-    combine_store<V, VEC, EVE, DX, ACC>(accw, p.ws + static_cast<int64_t>(blockIdx.x) * p.ldws,
-                                        part, r, R, t, T, N, team_stride);
-  }
-  if constexpr (CDB) {
-    if constexpr (CDW && ACC == 0) __syncthreads();  // the register path reuses `part`
-    combine_store<V, VEC, EVE, DX, ACC>(
-        accb, p.ws + (static_cast<int64_t>(CDW ? p.P : 0) + blockIdx.x) * p.ldws, part, r, R, t, T,
-        N, team_stride);
+  float* const dst_w = p.ws + static_cast<int64_t>(blockIdx.x) * p.ldws;
+  float* const dst_b = p.ws + (static_cast<int64_t>(CDW ? p.P : 0) + blockIdx.x) * p.ldws;
+  if constexpr (NG > 0 && ACC == 1) {
+    __syncthreads();  // every team's LDS rows are complete
+    if constexpr (CDW) combine_lds<V, VEC, EVE, DX>(part, dst_w, r, R, t, T, N, team_stride);
+    if constexpr (CDB)
+      combine_lds<V, VEC, EVE, DX>(part + (CDW ? T * V : 0), dst_b, r, R, t, T, N, team_stride);
+  } else {
+    if constexpr (CDW) combine_regs<V, VEC, EVE, DX>(accw, dst_w, part, r, R, t, T, N);
+    if constexpr (CDB) {
+      if constexpr (CDW) __syncthreads();  // `part` is reused
+      combine_regs<V, VEC, EVE, DX>(accb, dst_b, part, r, R, t, T, N);
+    }
   }
 }
 
