@@ -163,14 +163,13 @@ Shape plan(int kind, int64_t M, int64_t N, int xt, int ngrads = 0) {
   const int r_cap = wg_cap / s.team;
   int R;
   if (kind == 1) {
-    const size_t per_team = static_cast<size_t>(ngrads) * s.v * s.team * sizeof(float);
-    if (per_team <= kLdsBudget) {
-      // accumulators in LDS: as many teams as the workgroup and the LDS allow
+    // LDS accumulators: one [V][wg_cap] fp32 block per gradient, whatever R is
+    const size_t block = static_cast<size_t>(ngrads) * s.v * wg_cap * sizeof(float);
+    if (block <= kLdsBudget) {
       s.acc = 1;
-      const int r_lds = static_cast<int>(kLdsBudget / per_team);
-      R = o.rows ? o.rows : std::min(r_cap, r_lds);
-      R = std::max(1, std::min({R, r_cap, r_lds}));
-      s.shmem = static_cast<size_t>(R) * per_team;
+      R = o.rows ? o.rows : r_cap;
+      R = std::max(1, std::min(R, r_cap));
+      s.shmem = block;
     } else {
       // accumulators in VGPRs; LDS only for the final team combine
       s.acc = 0;

@@ -252,40 +252,41 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
 // Parameter-gradient accumulators of one thread: V fp32 partial sums over the rows a
 // team has processed, for the thread's V columns.  Two homes:
 //   ACC = 0: registers (V VGPRs per gradient).
-//   ACC = 1: the workgroup's LDS, one private row of T*V floats per team and gradient
-//            (layout [group of 4 elements][thread][4]: every access is a conflict-free
-//            16-byte ds_read/ds_write).  Frees the VGPRs for more waves per SIMD.
-template <int V, int ACC> struct Acc {
+//   ACC = 1: the workgroup's LDS, a [V/4][S][4] block per gradient (S = the kernel's
+//            largest workgroup): group j (elements 4j .. 4j+3) of workgroup thread tid
+//            is the float4 at j * S + tid.  Each group is one 16-byte read-modify-write;
+//            a wave's 64 lanes cover 1 KiB of consecutive words (no bank conflict),
+//            and j * S * 16 is an immediate offset from one base register, so the
+//            compiler sees that the groups do not overlap and can overlap their reads.
+//            Only this thread touches its float4s: deterministic sums.
+// Both add with one rounding: acc = fma(a, b, acc).
+template <int V, int ACC, int S> struct Acc {
   static_assert(V % 4 == 0, "accumulators are kept in groups of four");
   float reg[ACC == 0 ? V : 1];
-  float* lds;  // this thread's base: team row + 4 * t
-  int T;
+  float4* lds;  // ACC = 1: this thread's group 0
 
-  __device__ __forceinline__ void init(float* team_row, int t, int T_) {
-    T = T_;
+  __device__ __forceinline__ void init(float* block, int tid) {
     if constexpr (ACC == 0) {
 #pragma unroll
       for (int i = 0; i < V; ++i) reg[i] = 0.0f;
     } else {
-      lds = team_row + 4 * t;
+      lds = reinterpret_cast<float4*>(block) + tid;
 #pragma unroll
-      for (int j = 0; j < V / 4; ++j)
-        *reinterpret_cast<float4*>(lds + 4 * j * T) = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < V / 4; ++j) lds[j * S] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  // acc[4j .. 4j+3] += a[k] * b[k], one fused multiply-add each
+  // acc[4j + k] += a[k] * b[k]
   __device__ __forceinline__ void add4(int j, const float (&a)[4], const float (&b)[4]) {
     if constexpr (ACC == 0) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) reg[4 * j + k] = fmaf(a[k], b[k], reg[4 * j + k]);
     } else {
-      float4* p = reinterpret_cast<float4*>(lds + 4 * j * T);
-      float4 v = *p;
+      float4 v = lds[j * S];
       v.x = fmaf(a[0], b[0], v.x);
       v.y = fmaf(a[1], b[1], v.y);
       v.z = fmaf(a[2], b[2], v.z);
       v.w = fmaf(a[3], b[3], v.w);
-      *p = v;
+      lds[j * S] = v;
     }
   }
   __device__ __forceinline__ float get(int i) const { return reg[i]; }  // ACC = 0
@@ -294,8 +295,8 @@ template <int V, int ACC> struct Acc {
 // Register accumulators (ACC = 0): the R teams' sums are added in team order through
 // `part` and team 0 writes the workgroup's partial row `dst` (columns past N are not
 // written).
-template <int V, bool VEC, int EVE, int DX>
-__device__ __forceinline__ void combine_regs(const Acc<V, 0>& acc, float* dst, float* part, int r,
+template <int V, bool VEC, int EVE, int DX, int S>
+__device__ __forceinline__ void combine_regs(const Acc<V, 0, S>& acc, float* dst, float* part, int r,
                                              int R, int t, int T, int N) {
   using FX = Frag<DX, V, EVE, VEC>;
   float tot[V];
@@ -325,18 +326,19 @@ __device__ __forceinline__ void combine_regs(const Acc<V, 0>& acc, float* dst, f
 
 // LDS accumulators (ACC = 1): every team takes part.  Team r handles the groups of four
 // elements j = r, r + R, ...; for each, thread t adds the R teams' float4 in team order
-// (16-byte, conflict-free LDS reads) and writes the four columns of the partial row
-// `dst`.  The sums are the same as adding the teams' rows element by element in team
-// order.  The caller has synchronised the workgroup after the last accumulation.
-template <int V, bool VEC, int EVE, int DX>
-__device__ __forceinline__ void combine_lds(const float* rows, float* dst, int r, int R, int t,
-                                            int T, int N, int team_stride) {
+// (16-byte reads of consecutive words) and writes the group's four columns with one
+// 16-byte store.  The caller has synchronised the workgroup after the last
+// accumulation.
+template <int V, bool VEC, int EVE, int DX, int S>
+__device__ __forceinline__ void combine_lds(const float* block, float* dst, int r, int R, int t,
+                                            int T, int N) {
   using FX = Frag<DX, V, EVE, VEC>;
+  const float4* b4 = reinterpret_cast<const float4*>(block);
   for (int j = r; j < V / 4; j += R) {
-    const float* src = rows + 4 * (j * T + t);
-    float4 a = *reinterpret_cast<const float4*>(src);
+    const float4* src = b4 + j * S + t;
+    float4 a = src[0];
     for (int q = 1; q < R; ++q) {
-      const float4 b = *reinterpret_cast<const float4*>(src + q * team_stride);
+      const float4 b = src[q * T];
       a.x += b.x;
       a.y += b.y;
       a.z += b.z;
@@ -400,11 +402,11 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
 #pragma unroll
     for (int i = 0; i < V; ++i) wv[i] = wf.get(i);
   }
-  // LDS accumulator rows: [team][gradient][T * V]
-  const int team_stride = NG * T * V;
-  Acc<V, ACC> accw, accb;
-  if constexpr (CDW) accw.init(part + r * team_stride, t, T);
-  if constexpr (CDB) accb.init(part + r * team_stride + (CDW ? T * V : 0), t, T);
+  // LDS accumulator blocks: [gradient][V/4][S][4]
+  constexpr int S = bwd_max_wg(V, Ty<DX>::B);
+  Acc<V, ACC, S> accw, accb;
+  if constexpr (CDW) accw.init(part, tid);
+  if constexpr (CDB) accb.init(part + (CDW ? V * S : 0), tid);
 
   const int64_t row_end = p.M;
   const int iters = (p.rows_per_wg + R - 1) / R;
@@ -562,15 +564,14 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   float* const dst_w = p.ws + static_cast<int64_t>(blockIdx.x) * p.ldws;
   float* const dst_b = p.ws + (static_cast<int64_t>(CDW ? p.P : 0) + blockIdx.x) * p.ldws;
   if constexpr (NG > 0 && ACC == 1) {
-    __syncthreads();  // every team's LDS rows are complete
-    if constexpr (CDW) combine_lds<V, VEC, EVE, DX>(part, dst_w, r, R, t, T, N, team_stride);
-    if constexpr (CDB)
-      combine_lds<V, VEC, EVE, DX>(part + (CDW ? T * V : 0), dst_b, r, R, t, T, N, team_stride);
+    __syncthreads();  // every accumulation has landed
+    if constexpr (CDW) combine_lds<V, VEC, EVE, DX, S>(part, dst_w, r, R, t, T, N);
+    if constexpr (CDB) combine_lds<V, VEC, EVE, DX, S>(part + (CDW ? V * S : 0), dst_b, r, R, t, T, N);
   } else {
-    if constexpr (CDW) combine_regs<V, VEC, EVE, DX>(accw, dst_w, part, r, R, t, T, N);
+    if constexpr (CDW) combine_regs<V, VEC, EVE, DX, S>(accw, dst_w, part, r, R, t, T, N);
     if constexpr (CDB) {
       if constexpr (CDW) __syncthreads();  // `part` is reused
-      combine_regs<V, VEC, EVE, DX>(accb, dst_b, part, r, R, t, T, N);
+      combine_regs<V, VEC, EVE, DX, S>(accb, dst_b, part, r, R, t, T, N);
     }
   }
 }

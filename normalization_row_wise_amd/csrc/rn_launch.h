@@ -31,7 +31,7 @@ bool launch_fwd_rms(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream
 bool launch_fwd_ln(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
 bool launch_fwd_fadd(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
 // Backward variants: xg = exact fp32 product g = dy * w (16-bit weight, no offset);
-// acc = 1 keeps the dw / db accumulators in LDS, 0 in registers (V >= 32 only).
+// acc = 1 keeps the dw / db accumulators in LDS, 0 in registers (V = 48 only).
 struct BwdVariant {
   bool cdw, cdb, xg;
   int acc;
@@ -61,8 +61,8 @@ inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
 
 template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, int ACC, int V>
 inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
-  if constexpr (ACC == 0 && (CDW || CDB) && V < 32) {
-    return false;  // narrow rows always fit their accumulators in LDS
+  if constexpr (ACC == 0 && (CDW || CDB) && V < 48) {
+    return false;  // up to V = 32 the LDS accumulator blocks always fit
   } else {
     auto k = l.vec ? bwd_kernel<OP, DX, DW, V, true, CDW, CDB, XG, ACC>
                    : bwd_kernel<OP, DX, DW, V, false, CDW, CDB, XG, ACC>;
