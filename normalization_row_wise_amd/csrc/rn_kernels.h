@@ -118,28 +118,22 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
   const uint32_t row_bytes = static_cast<uint32_t>(N) * Ty<DX>::B;
   const uint32_t par_bytes = static_cast<uint32_t>(N) * Ty<DW>::B;
 
-  // Parameters of this thread's columns, loaded once per workgroup.
-  float wv[V];
-  float bv[OP == OP_LN ? V : 1];
-  {
-    FW wf;
-    wf.load(make_rsrc(p.w, par_bytes), t, T);
+  // Parameters of this thread's columns, loaded once per workgroup.  LayerNorm keeps w
+  // and b as loaded (16-bit words are unpacked on use: half the VGPRs of fp32 copies,
+  // which lets the bf16 instance run four waves per SIMD); the RMS forms hold
+  // w + offset in fp32.
+  float wv[OP == OP_LN ? 1 : V];
+  FW wf, bf;
+  wf.load(make_rsrc(p.w, par_bytes), t, T);
+  if constexpr (OP == OP_LN) {
+    if (p.b != nullptr)
+      bf.load(make_rsrc(p.b, par_bytes), t, T);
+    else
+      bf.zero();
+  } else {
+    // [gemma] Summary: offset added to the weight in fp32, inside the kernel.
 #pragma unroll
-    for (int i = 0; i < V; ++i) wv[i] = wf.get(i);
-    if constexpr (OP == OP_LN) {
-      if (p.b != nullptr) {
-        wf.load(make_rsrc(p.b, par_bytes), t, T);
-#pragma unroll
-        for (int i = 0; i < V; ++i) bv[i] = wf.get(i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) bv[i] = 0.0f;
-      }
-    } else {
-      // [gemma] Summary: offset added to the weight in fp32, inside the kernel.
-#pragma unroll
-      for (int i = 0; i < V; ++i) wv[i] = wv[i] + p.offset;
-    }
+    for (int i = 0; i < V; ++i) wv[i] = wf.get(i) + p.offset;
   }
 
   const int64_t row_end = p.M;
@@ -169,8 +163,12 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
   auto process = [&](In& in, int it) {
     const int64_t row = row_of(it);
     const bool valid = row < row_end;
-    opaque<V>(wv);
-    if constexpr (OP == OP_LN) opaque<V>(bv);
+    if constexpr (OP == OP_LN) {
+      wf.opaque();
+      bf.opaque();
+    } else {
+      opaque<V>(wv);
+    }
     FX& xf = in.x;
     if constexpr (OP == OP_FADD) {
       float s[V];
@@ -215,7 +213,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
       for (int i = 0; i < V; ++i) {
         const double e = static_cast<double>(xf.get(i)) - mean;
         o[i] = static_cast<float>(
-            fma(e * rstd, static_cast<double>(wv[i]), static_cast<double>(bv[i])));
+            fma(e * rstd, static_cast<double>(wf.get(i)), static_cast<double>(bf.get(i))));
       }
       if (valid && t == 0) {
         if (p.rstd != nullptr) p.rstd[row] = static_cast<float>(rstd);
@@ -395,13 +393,28 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   const double off = (OP == OP_LN) ? 0.0 : static_cast<double>(p.offset);
 
   const uint32_t row_bytes = static_cast<uint32_t>(N) * Ty<DX>::B;
-  float wv[V];
-  {
-    FW wf;
-    wf.load(make_rsrc(p.w, static_cast<uint32_t>(N) * Ty<DW>::B), t, T);
+  // The weight of this thread's columns.  Frozen instances keep it as loaded (16-bit
+  // words unpacked on use: half the VGPRs of an fp32 copy, so more waves per SIMD); the
+  // trainable ones, whose extra dW work makes them short of VALU issue rather than of
+  // waves, keep an fp32 copy and save the unpacking.
+  constexpr bool PACKW = NG == 0;
+  FW wf;
+  float wv[PACKW ? 1 : V];
+  wf.load(make_rsrc(p.w, static_cast<uint32_t>(N) * Ty<DW>::B), t, T);
+  if constexpr (!PACKW) {
 #pragma unroll
     for (int i = 0; i < V; ++i) wv[i] = wf.get(i);
   }
+  auto wget = [&](int i) -> float {
+    if constexpr (PACKW) return wf.get(i);
+    else return wv[i];
+  };
+  // Hide the weight's provenance at these points (see Frag::opaque); the fp32 copy is
+  // refreshed once per row, the packed words also after the row reduction.
+  auto wopaque = [&](bool after_reduction) {
+    if constexpr (PACKW) wf.opaque();
+    else if (!after_reduction) opaque<V>(wv);
+  };
   // LDS accumulator blocks: [gradient][V/4][S][4]
   constexpr int S = bwd_max_wg(V, Ty<DX>::B);
   Acc<V, ACC, S> accw, accb;
@@ -414,11 +427,11 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   // g = dy * (w + offset) in fp64 (the offset sum formed exactly), or the exact fp32
   // product when XG.
   auto gval = [&](float dys, int i) -> double {
-    if constexpr (XG) return static_cast<double>(dys * wv[i]);
-    else if constexpr (OP == OP_LN) return static_cast<double>(dys) * static_cast<double>(wv[i]);
+    if constexpr (XG) return static_cast<double>(dys * wget(i));
+    else if constexpr (OP == OP_LN) return static_cast<double>(dys) * static_cast<double>(wget(i));
     else {
       const double dyd = static_cast<double>(dys);
-      return fma(dyd, static_cast<double>(wv[i]), dyd * off);
+      return fma(dyd, static_cast<double>(wget(i)), dyd * off);
     }
   };
 
@@ -451,7 +464,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   auto process = [&](In& in, int it) {
     const int64_t row = row_of(it);
     const bool valid = row < row_end;
-    opaque<V>(wv);
+    wopaque(false);
     FX& gf = in.g;
     FX& xf = in.x;
     float o[V];
@@ -467,6 +480,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
       team_sum<2>(acc, wpr, wave0, red, parity);
       xf.opaque();
       gf.opaque();
+      wopaque(true);
       const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
       // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
       const double c = rstd * rstd * rstd * (acc[1] * inv_n);
@@ -504,6 +518,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
       team_sum<4>(acc, wpr, wave0, red, parity);
       xf.opaque();
       gf.opaque();
+      wopaque(true);
       acc[0] = fma(pad, K, acc[0]);          // zero-filled slots: d = -K, g = 0
       acc[1] = fma(-pad * K, K, acc[1]);
       const double delta = acc[0] * inv_n;   // mean - K
