@@ -11,13 +11,15 @@
 namespace rn {
 
 // ------------------------------------------------------------------------------------
-// Backward, stage 2: out[j] = sum over p = 0..P-1 of partial[p][j], in a fixed order
-// (thread slice s sums p = s, s + S, ... ascending; slices are then added in s order),
-// so dw / db are bitwise reproducible.  blockIdx.y picks dw (0) or db (1).
+// Backward, stage 2: out[j] = sum over p = 0..P-1 of partial[p][j], in a fixed order:
+// thread slice s sums p = s, s + 32, ... ascending, then the 32 slice sums are added as a
+// fixed binary tree (s + 16, then + 8, + 4, + 2, + 1), so dw / db are bitwise
+// reproducible.  blockIdx.y picks dw (0) or db (1).
 // ------------------------------------------------------------------------------------
 constexpr int CS_THREADS = 256;
 constexpr int CS_C4 = 8;                  // float4 columns per workgroup: one 128-byte line
 constexpr int CS_S = CS_THREADS / CS_C4;  // row slices per workgroup
+constexpr int CS_BATCH = 8;               // loads a thread keeps in flight
 
 __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const float* ws, int64_t ldws, int P,
                                                             int N, float* out0, float* out1) {
@@ -29,26 +31,36 @@ __global__ __launch_bounds__(CS_THREADS) void colsum_kernel(const float* ws, int
   const int c = (blockIdx.x * CS_C4 + ci) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (c < N) {
-#pragma unroll 4
-    for (int q = s; q < P; q += CS_S) {
-      const float4 v = *reinterpret_cast<const float4*>(src + static_cast<int64_t>(q) * ldws + c);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+    const float* col = src + c;
+    for (int q0 = s; q0 < P; q0 += CS_S * CS_BATCH) {
+      float4 v[CS_BATCH];
+#pragma unroll
+      for (int k = 0; k < CS_BATCH; ++k) {
+        const int q = q0 + k * CS_S;
+        v[k] = q < P ? *reinterpret_cast<const float4*>(col + static_cast<int64_t>(q) * ldws)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < CS_BATCH; ++k) {
+        acc.x += v[k].x;
+        acc.y += v[k].y;
+        acc.z += v[k].z;
+        acc.w += v[k].w;
+      }
     }
   }
   sh[s][ci] = acc;
-  __syncthreads();
-  if (s == 0 && c < N) {
-    float4 tot = sh[0][ci];
-    for (int q = 1; q < CS_S; ++q) {
-      const float4 v = sh[q][ci];
-      tot.x += v.x;
-      tot.y += v.y;
-      tot.z += v.z;
-      tot.w += v.w;
+#pragma unroll
+  for (int h = CS_S / 2; h >= 1; h /= 2) {
+    __syncthreads();
+    if (s < h) {
+      const float4 a = sh[s][ci];
+      const float4 b = sh[s + h][ci];
+      sh[s][ci] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
     }
+  }
+  if (s == 0 && c < N) {
+    const float4 tot = sh[0][ci];
     out[c] = tot.x;
     if (c + 1 < N) out[c + 1] = tot.y;
     if (c + 2 < N) out[c + 2] = tot.z;
