@@ -263,21 +263,26 @@ template <int V, int ACC, int S> struct Acc {
   float reg[ACC == 0 ? V : 1];
   float4* lds;  // ACC = 1: this thread's group 0
 
+  // ACC = 1 needs no zeroing: the first pass stores instead of adding (`first`).
   __device__ __forceinline__ void init(float* block, int tid) {
     if constexpr (ACC == 0) {
 #pragma unroll
       for (int i = 0; i < V; ++i) reg[i] = 0.0f;
     } else {
       lds = reinterpret_cast<float4*>(block) + tid;
-#pragma unroll
-      for (int j = 0; j < V / 4; ++j) lds[j * S] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
-  // acc[4j + k] += a[k] * b[k]
-  __device__ __forceinline__ void add4(int j, const float (&a)[4], const float (&b)[4]) {
+  // acc[4j + k] += a[k] * b[k]; on the workgroup's first pass (uniform) the LDS copy is
+  // written as fma(a, b, 0), the same value an add to a zeroed accumulator gives, which
+  // saves the zeroing pass and one read.
+  __device__ __forceinline__ void add4(int j, const float (&a)[4], const float (&b)[4],
+                                       bool first) {
     if constexpr (ACC == 0) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) reg[4 * j + k] = fmaf(a[k], b[k], reg[4 * j + k]);
+    } else if (first) {
+      lds[j * S] = make_float4(fmaf(a[0], b[0], 0.0f), fmaf(a[1], b[1], 0.0f),
+                               fmaf(a[2], b[2], 0.0f), fmaf(a[3], b[3], 0.0f));
     } else {
       float4 v = lds[j * S];
       v.x = fmaf(a[0], b[0], v.x);
@@ -501,7 +506,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
           dyv[k] = dys;
           xh[k] = xs * rs;
         }
-        if constexpr (CDW) accw.add4(j, dyv, xh);
+        if constexpr (CDW) accw.add4(j, dyv, xh, it == 0);
       }
     } else {  // LayerNorm
       const double K = in.k;
@@ -546,8 +551,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
           dyv[k] = dys;
           xh[k] = fmaf(xs, rs, nmr);
         }
-        if constexpr (CDW) accw.add4(j, dyv, xh);
-        if constexpr (CDB) accb.add4(j, dyv, one);
+        if constexpr (CDW) accw.add4(j, dyv, xh, it == 0);
+        if constexpr (CDB) accb.add4(j, dyv, one, it == 0);
       }
     }
     FX of;
