@@ -146,9 +146,15 @@ class Sets:
         self.bwd((k + self.S // 2) % self.S)
 
 
+MAX_SETS = 256
+
+
 def n_sets(bytes_per_set: int) -> int:
+    """Buffer sets to rotate through: more than three times the MALL in total, so every
+    step reads data evicted from L2 and MALL.  Capped at MAX_SETS: a problem too small to
+    reach that (a single decode row) is timed with its sets partly cache-resident."""
     s = 2
-    while s * bytes_per_set < 3 * MALL_BYTES:
+    while s * bytes_per_set < 3 * MALL_BYTES and s < MAX_SETS:
         s += 2
     return max(s, 4)
 
@@ -160,8 +166,8 @@ def time_steps(sets, K, W, use_graph, torch):
         sets.step(k)
     torch.cuda.synchronize()
     if use_graph:
-        G = min(K, max(sets.S, 64))
-        G -= G % sets.S
+        # one graph holds a whole number of passes over the sets, at least 64 steps
+        G = sets.S * max(1, -(-64 // sets.S))
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -300,6 +306,7 @@ def main():
     trainable = not args.frozen
     probe = Sets(wl, 1, trainable, rn, torch)
     S = n_sets(probe.bytes_per_set)
+    cold = S * probe.bytes_per_set >= 3 * MALL_BYTES
     del probe
     sets = Sets(wl, S, trainable, rn, torch)
 
@@ -338,7 +345,8 @@ def main():
         "data": "synthetic (seeded CPU randn, no dataset)",
         "config": {"workload": wl.name, "op": wl.op, "M": wl.M, "N": wl.N, "io": wl.io,
                    "weight": wl.wt, "trainable_params": trainable,
-                   "timing": "eager" if args.eager else "hip graph replay", "buffer_sets": S},
+                   "timing": "eager" if args.eager else "hip graph replay", "buffer_sets": S,
+                   "inputs_cold_in_mall": cold},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_per_call": {"fwd_kernel": round(ev["fwd_us_median"], 3),
                         "bwd_stage1_kernel": round(ev["bwd_stage1_us_median"], 3),

@@ -74,7 +74,10 @@ typedef enum rn_status {
 /* Bytes of workspace a backward call needs for `n_param_grads` (0, 1 or 2) fp32
  * parameter gradients at this shape: per-workgroup partial rows of dw / db,
  * reduced by a second kernel in fixed order.  0 when n_param_grads == 0 (frozen
- * parameters need no workspace: [frozen], Motivation).  Returns 0 for invalid shapes. */
+ * parameters need no workspace: [frozen], Motivation).  Returns 0 for invalid shapes.
+ * When a single workgroup covers every row (very small M) and dw / db are 16-byte
+ * aligned, the gradients are written directly and the workspace is left untouched;
+ * it must still be passed. */
 size_t rn_bwd_workspace_bytes(int64_t M, int64_t N, int n_param_grads);
 
 /* RMSNorm forward.  [gemma] Summary: offset added to the weight in fp32 in-kernel.

@@ -376,7 +376,14 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   BwdArgs a{};
   a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
   a.dx = dx; a.lddx = lddx;
-  a.ws = static_cast<float*>(ws); a.ldws = ldws; a.P = s.P;
+  // One workgroup covering every row (a decode row, say): its combined row is the
+  // gradient itself, written in place of a partial row, and no column sum is launched.
+  // The kernel writes 16-byte groups, so this needs 16-byte aligned outputs.
+  const bool direct = s.P == 1 && aligned16(dw) && aligned16(db);
+  float* const part = static_cast<float*>(ws);
+  a.pw = direct ? dw : part;
+  a.pb = direct ? db : part + (dw != nullptr ? static_cast<int64_t>(s.P) * ldws : 0);
+  a.ldws = ldws;
   a.M = M; a.N = static_cast<int>(N); a.team = s.team;
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
@@ -392,7 +399,7 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   else ok = launch_bwd_fadd(dxt, dwt, bv, l, a, st);
   if (!ok) return RN_ERR_DTYPE;
   if ((e = launched()) != RN_OK) return e;
-  if (ngrads == 0) return RN_OK;  // frozen: no partials, no second kernel
+  if (ngrads == 0 || direct) return RN_OK;  // frozen, or the gradient written directly
   return colsum(static_cast<const float*>(ws), ldws, s.P, N, dw, db, st);
 }
 

@@ -48,7 +48,8 @@ struct BwdArgs {
   const void* dres; int64_t lddr;   // fused add: gradient reaching residual_out, may be null
   const void* w;
   void* dx; int64_t lddx;
-  float* ws; int64_t ldws; int P;   // partial rows: [P][ldws] for dw, then [P][ldws] for db
+  float* pw; float* pb; int64_t ldws;  // partial rows of dw and db: [P][ldws] each (when one
+                                       // workgroup covers every row: dw and db themselves)
   int64_t M; int N; int team; int rows_per_wg;
   float eps, offset;
 };
@@ -581,8 +582,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     }
   }
 
-  float* const dst_w = p.ws + static_cast<int64_t>(blockIdx.x) * p.ldws;
-  float* const dst_b = p.ws + (static_cast<int64_t>(CDW ? p.P : 0) + blockIdx.x) * p.ldws;
+  float* const dst_w = CDW ? p.pw + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
+  float* const dst_b = CDB ? p.pb + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
   if constexpr (NG > 0 && ACC == 1) {
     __syncthreads();  // every accumulation has landed
     if constexpr (CDW) combine_lds<V, VEC, EVE, DX, S>(part, dst_w, r, R, t, T, N);

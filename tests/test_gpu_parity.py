@@ -228,3 +228,43 @@ def test_errors_do_not_launch_on_device():
     ws = torch.empty(8, dtype=torch.uint8, device=gp.dev())
     with pytest.raises(rn.RowNormError):
         rn.rmsnorm_bwd(x, x, w.to(torch.bfloat16), workspace=ws)
+
+
+# ---- one workgroup covering every row: the gradient is written without a column sum ----
+
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("m", [1, 3])
+def test_single_workgroup_gradient_direct_and_via_workspace(op, m):
+    import normalization_row_wise_amd as rn
+    _say("direct gradient", op, m)
+    wl = workloads.small(op, m, 18432 if op == "rmsnorm" else 4096, "bf16",
+                         offset=1.0 if op != "layernorm" else 0.0,
+                         weight="gemma" if op != "layernorm" else "unit", seed=60 + m)
+    t = workloads.generate(wl)
+    d = gp.to_device(t)
+    N = wl.N
+    aligned = {"dw": torch.full((N,), 7.0, device=gp.dev())}
+    buf = torch.full((2 * N + 8,), 7.0, device=gp.dev())
+    shifted = {"dw": buf[1:1 + N]}                  # 4-byte aligned only: workspace path
+    if op == "layernorm":
+        aligned["db"] = torch.full((N,), 7.0, device=gp.dev())
+        shifted["db"] = buf[N + 5:2 * N + 5]
+    outs = []
+    for o in (aligned, shifted):
+        if op == "rmsnorm":
+            rn.rmsnorm_bwd(d["dy"], d["x"], d["w"], t["eps"], t["offset"], dw=o["dw"])
+        elif op == "layernorm":
+            rn.layernorm_bwd(d["dy"], d["x"], d["w"], t["eps"], dw=o["dw"], db=o["db"])
+        else:
+            _, ro, _ = rn.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["w"], t["eps"],
+                                                t["offset"])
+            rn.fused_add_rmsnorm_bwd(d["dy"], ro, d["w"], t["eps"], t["offset"], d["dres"],
+                                     dw=o["dw"])
+        outs.append(o)
+    torch.cuda.synchronize()
+    ref = gp.run_oracle(wl, t)
+    for k in outs[0]:
+        a, b = outs[0][k] + 0.0, outs[1][k] + 0.0      # +0.0 folds a signed zero
+        assert torch.equal(a, b), k
+        assert gp.f32_report(a.cpu(), ref[k]) <= gp.REL_GRAD, k
+    assert torch.all(buf[0] == 7.0) and torch.all(buf[1 + N:N + 5] == 7.0)
