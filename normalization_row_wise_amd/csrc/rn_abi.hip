@@ -76,10 +76,15 @@ namespace {
 
 // At most this many partial rows per parameter gradient.  The row-to-workgroup split
 // depends only on (M, N), never on the device, so dw / db are bitwise reproducible.
+// Rows of at most kNarrowN elements have small partial rows, and take more of them so
+// that their many short rows spread over more workgroups.
 #ifndef RN_MAX_PARTIALS
 #define RN_MAX_PARTIALS 256
 #endif
 constexpr int64_t kMaxPartials = RN_MAX_PARTIALS;
+constexpr int64_t kNarrowN = 256;
+constexpr int64_t kMaxPartialsNarrow = 512;
+inline int64_t max_partials(int64_t N) { return N <= kNarrowN ? kMaxPartialsNarrow : kMaxPartials; }
 // Dynamic LDS a backward workgroup may use (gfx950 has 160 KiB per CU; 1 KiB is
 // taken by the static row-reduction slots).
 #ifndef RN_LDS_BUDGET
@@ -153,6 +158,7 @@ inline int pick_v(int kind, int op, int64_t N, int eb, int requested) {
 struct Shape {
   int v = 0;
   int team = 0;
+  int ts = 0;              // sub-wave team width (0: teams of whole waves)
   int R = 1;               // teams per workgroup
   int64_t rows_per_wg = 1;
   int64_t grid = 0;
@@ -166,12 +172,48 @@ struct Shape {
 // for 8192 x 8192 bf16: 46.0 us against 48.6 at four rows and 46.4 at one).
 constexpr int64_t kTargetGrid = 4096;
 
+// Narrow rows (N <= kNarrowN, 16-byte accesses possible): teams of 8, 16 or 32 lanes,
+// several rows per wave, 8 elements per lane.  The workgroup's block of rows must stay
+// addressable with 32-bit offsets (R rows of the widest row stride).  0: not narrow.
+inline int narrow_team(int64_t N, bool vec, int64_t max_ld, int eb) {
+  if (!vec || N > kNarrowN) return 0;
+  const int ts = N <= 64 ? 8 : (N <= 128 ? 16 : 32);
+  const int64_t r_max = 512 / ts;
+  if (r_max * std::max(max_ld, N) * eb >= (int64_t(1) << 31)) return 0;
+  return ts;
+}
+
 // kind: 0 forward, 1 backward with parameter grads, 2 backward without.
-// ngrads: parameter gradients computed (kind 1).
-Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads = 0) {
+// ngrads: parameter gradients computed (kind 1).  vec: 16-byte accesses possible;
+// max_ld: the widest row stride of the call's row tensors.
+Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec, int64_t max_ld) {
   Shape s;
   const Override& o = g_override[kind];
   const int eb = elem_bytes(xt);
+  if (const int ts = o.v ? 0 : narrow_team(N, vec, max_ld, eb)) {
+    s.v = 8;
+    s.team = ts;
+    s.ts = ts;
+    const int wg = kind == 1 ? 512 : 256;  // 512 = the LDS accumulator stride
+    s.R = wg / ts;
+    const int64_t R = s.R;
+    int64_t rows;
+    if (kind == 1) {
+      s.acc = 1;
+      s.shmem = static_cast<size_t>(ngrads) * 8 * 512 * sizeof(float);
+      rows = cdiv(cdiv(M, R), max_partials(N)) * R;
+    } else if (kind == 2) {
+      rows = R;
+    } else {
+      rows = round_up(cdiv(M, kTargetGrid), R);
+    }
+    if (o.wg_rows && kind != 1) rows = round_up(o.wg_rows, R);
+    rows = std::max<int64_t>(rows, round_up(cdiv(M, int64_t(1) << 30), R));
+    s.rows_per_wg = rows;
+    s.grid = M > 0 ? cdiv(M, rows) : 0;
+    s.P = kind == 1 ? static_cast<int>(s.grid) : 0;
+    return s;
+  }
   s.v = pick_v(kind, op, N, eb, o.v);
   s.team = static_cast<int>(team_of(N, s.v));
   const int wg_cap = max_wg(kind, s.v, eb);
@@ -204,8 +246,9 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads = 0) {
   s.R = R;
   if (kind == 1) {
     const int64_t groups = cdiv(M, R);
-    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : cdiv(groups, kMaxPartials) * R;
-    if (cdiv(M, rows) > std::min<int64_t>(M, kMaxPartials)) rows = cdiv(groups, kMaxPartials) * R;
+    const int64_t pmax = max_partials(N);
+    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : cdiv(groups, pmax) * R;
+    if (cdiv(M, rows) > std::min<int64_t>(M, pmax)) rows = cdiv(groups, pmax) * R;
     s.rows_per_wg = std::max<int64_t>(rows, R);
     s.P = static_cast<int>(M > 0 ? cdiv(M, s.rows_per_wg) : 0);
     s.grid = s.P;
@@ -241,7 +284,7 @@ extern "C" {
 
 size_t rn_bwd_workspace_bytes(int64_t M, int64_t N, int n_param_grads) {
   if (check_shape(M, N) != RN_OK || n_param_grads <= 0 || n_param_grads > 2) return 0;
-  return static_cast<size_t>(n_param_grads) * static_cast<size_t>(std::min(M, kMaxPartials)) *
+  return static_cast<size_t>(n_param_grads) * static_cast<size_t>(std::min(M, max_partials(N))) *
          static_cast<size_t>(ldws_of(N)) * sizeof(float);
 }
 
@@ -302,15 +345,17 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
              aligned16(w) && (b == nullptr || aligned16(b));
   if (op == OP_FADD) vec = vec && vec_ok(res, ldr, M, eb) && vec_ok(ro, ldro, M, eb);
 
-  const Shape s = plan(0, op, M, N, xt);
+  int64_t max_ld = std::max(ldx, ldy);
+  if (op == OP_FADD) max_ld = std::max({max_ld, ldr, ldro});
+  const Shape s = plan(0, op, M, N, xt, 0, vec, M > 1 ? max_ld : N);
   FwdArgs a{};
   a.x = x; a.ldx = ldx; a.res = res; a.ldr = ldr; a.w = w; a.b = b;
   a.y = y; a.ldy = ldy; a.ro = ro; a.ldro = ldro; a.rstd = rstd; a.mean = mean;
   a.M = M; a.N = static_cast<int>(N); a.team = s.team;
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
-  Launch l{s.v, vec, dim3(static_cast<unsigned>(s.grid)), dim3(static_cast<unsigned>(s.R * s.team)),
-           0, g_timing[0][0], g_timing[0][1]};
+  Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
+           dim3(static_cast<unsigned>(s.R * s.team)), 0, g_timing[0][0], g_timing[0][1]};
   bool ok = false;
   const int dx = to_dt(xt), dw = to_dt(wt);
   if (op == OP_RMS) ok = launch_fwd_rms(dx, dw, l, a, st);
@@ -372,7 +417,9 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   const bool vec = (N % ve) == 0 && vec_ok(dy, lddy, M, eb) && vec_ok(x, ldx, M, eb) &&
                    vec_ok(dx, lddx, M, eb) && vec_ok(dres, lddr, M, eb) && aligned16(w);
 
-  const Shape s = plan(ngrads > 0 ? 1 : 2, op, M, N, xt, ngrads);
+  int64_t max_ld = std::max({lddy, ldx, lddx});
+  if (dres != nullptr) max_ld = std::max(max_ld, lddr);
+  const Shape s = plan(ngrads > 0 ? 1 : 2, op, M, N, xt, ngrads, vec, M > 1 ? max_ld : N);
   BwdArgs a{};
   a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
   a.dx = dx; a.lddx = lddx;
@@ -387,8 +434,8 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   a.M = M; a.N = static_cast<int>(N); a.team = s.team;
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
-  Launch l{s.v, vec, dim3(static_cast<unsigned>(s.grid)), dim3(static_cast<unsigned>(s.R * s.team)),
-           s.shmem, g_timing[1][0], g_timing[1][1]};
+  Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
+           dim3(static_cast<unsigned>(s.R * s.team)), s.shmem, g_timing[1][0], g_timing[1][1]};
   bool ok = false;
   const int dxt = to_dt(xt), dwt = to_dt(wt);
   // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it

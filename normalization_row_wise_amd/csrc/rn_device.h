@@ -133,6 +133,54 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
     }
   }
 
+  // Several rows per wave (teams narrower than a wave): `rs` covers a block of rows,
+  // `base` is this lane's row offset in bytes, and accesses at or past column N are
+  // pushed out of the resource, so they read zero and are not stored.  (Vector path: N
+  // is a multiple of VE, so an access is wholly inside the row or wholly outside.)
+  static __device__ __forceinline__ uint32_t off_at(int l, uint32_t base, int t, int T, int N) {
+    const int col = (l * T + t) * VE;
+    return col < N ? base + static_cast<uint32_t>(col * B) : 0x80000000u;
+  }
+  __device__ __forceinline__ void load_at(rsrc_t rs, uint32_t base, int t, int T, int N) {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const uint32_t off = off_at(l, base, t, T, N);
+      if constexpr (VEC) {
+        static_assert(WPL % 4 == 0, "vector access is a whole number of 16-byte loads");
+#pragma unroll
+        for (int q = 0; q < WPL / 4; ++q) {
+          const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + q * 16, 0, 0);
+          w[l * WPL + q * 4 + 0] = v.x;
+          w[l * WPL + q * 4 + 1] = v.y;
+          w[l * WPL + q * 4 + 2] = v.z;
+          w[l * WPL + q * 4 + 3] = v.w;
+        }
+      } else if constexpr (B == 2) {
+        w[l] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+      } else {
+        w[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store_at(rsrc_t rs, uint32_t base, int t, int T, int N) const {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const uint32_t off = off_at(l, base, t, T, N);
+      if constexpr (VEC) {
+#pragma unroll
+        for (int q = 0; q < WPL / 4; ++q) {
+          const v4u v = {w[l * WPL + q * 4], w[l * WPL + q * 4 + 1], w[l * WPL + q * 4 + 2],
+                         w[l * WPL + q * 4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off + q * 16, 0, 0);
+        }
+      } else if constexpr (B == 2) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[l]), rs, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(w[l], rs, off, 0, 0);
+      }
+    }
+  }
+
   // Store the words as they are; stores past the resource's byte count are dropped.
   __device__ __forceinline__ void store_raw(rsrc_t rs, int t, int T) const {
 #pragma unroll
@@ -211,6 +259,35 @@ template <int NV> __device__ __forceinline__ void wave_sum(double (&v)[NV]) {
 #pragma unroll
   for (int j = 0; j < NV; ++j)
     v[j] = (read_lane(v[j], 0) + read_lane(v[j], 16)) + (read_lane(v[j], 32) + read_lane(v[j], 48));
+}
+
+// Sum over each aligned group of TS lanes (TS = 8, 16 or 32: teams narrower than a
+// wave, one row each); every lane of a group ends with the same bits.  Quad swaps give
+// every lane its quad's sum; row_half_mirror (lane i <-> 7 - i inside 8 lanes) pairs
+// the two quads of an 8-lane group, row_mirror (i <-> 15 - i) the two halves of a
+// 16-lane row -- each step adds the same two operands in both lanes of a pair.  For 32
+// lanes the four row sums are read as scalars and added in one fixed order.
+template <int TS, int NV> __device__ __forceinline__ void group_sum(double (&v)[NV]) {
+  static_assert(TS == 8 || TS == 16 || TS == 32, "sub-wave teams of 8, 16 or 32 lanes");
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0xB1>(v[j]);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0x4E>(v[j]);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0x141>(v[j]);
+  if constexpr (TS >= 16) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] += dpp_mov<0x140>(v[j]);
+  }
+  if constexpr (TS == 32) {
+    const bool hi = (threadIdx.x & 63) >= 32;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const double lo2 = read_lane(v[j], 0) + read_lane(v[j], 16);
+      const double hi2 = read_lane(v[j], 32) + read_lane(v[j], 48);
+      v[j] = hi ? hi2 : lo2;
+    }
+  }
 }
 
 // Sum over the team's waves.  `red` is a workgroup-shared [2][16][4] buffer used in

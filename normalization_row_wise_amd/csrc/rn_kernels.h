@@ -93,10 +93,65 @@ template <int DX> __device__ __forceinline__ double first_elem(rsrc_t rs) {
   return static_cast<double>(bits_to_f<DX>(b));
 }
 
+// Where one row of one tensor lives for this lane.  Whole-wave teams (TS = 0): a buffer
+// resource over exactly that row (rows are uniform per wave).  Teams narrower than a
+// wave (TS = 8, 16 or 32 lanes: several rows per wave): one resource over the
+// workgroup's block of rows for the pass, plus this lane's row offset; columns past N
+// are masked per access.  Either way rows past M read zeros and their stores vanish.
+struct RowAt {
+  rsrc_t rs;
+  uint32_t base;
+};
+
+template <typename SX, int TS>
+__device__ __forceinline__ RowAt row_at(const void* base, int64_t ld, int64_t row, int64_t row0,
+                                        int R, int r, int N, int64_t M) {
+  constexpr uint32_t B = sizeof(SX);
+  if constexpr (TS == 0) {
+    return {make_rsrc(static_cast<const SX*>(base) + row * ld,
+                      row < M ? static_cast<uint32_t>(N) * B : 0u), 0u};
+  } else {
+    // the block holds rows row0 .. row0 + R - 1; only the first nv exist
+    const int64_t nv = min(max(M - row0, int64_t(0)), static_cast<int64_t>(R));
+    const uint32_t bytes = nv > 0 ? static_cast<uint32_t>(((nv - 1) * ld + N) * B) : 0u;
+    return {make_rsrc(static_cast<const SX*>(base) + row0 * ld, bytes),
+            static_cast<uint32_t>(r * ld * B)};
+  }
+}
+
+template <int TS, typename F>
+__device__ __forceinline__ void frag_load(F& f, const RowAt& a, int t, int T, int N) {
+  if constexpr (TS == 0) f.load(a.rs, t, T);
+  else f.load_at(a.rs, a.base, t, T, N);
+}
+template <int TS, typename F>
+__device__ __forceinline__ void frag_store(const F& f, const RowAt& a, int t, int T, int N) {
+  if constexpr (TS == 0) f.store_raw(a.rs, t, T);
+  else f.store_at(a.rs, a.base, t, T, N);
+}
+// The row's first element (0 past the end).
+template <int DX, int TS> __device__ __forceinline__ double first_at(const RowAt& a) {
+  if constexpr (TS == 0) {
+    return first_elem<DX>(a.rs);
+  } else {
+    uint32_t b;
+    if constexpr (Ty<DX>::B == 2) b = __builtin_amdgcn_raw_buffer_load_b16(a.rs, a.base, 0, 0);
+    else b = __builtin_amdgcn_raw_buffer_load_b32(a.rs, a.base, 0, 0);
+    return static_cast<double>(bits_to_f<DX>(b));
+  }
+}
+// Row sums over the team: DPP inside a lane group, or across waves through LDS.
+template <int TS, int NV>
+__device__ __forceinline__ void row_sum(double (&v)[NV], int wpr, int wave0, double (*red)[16][4],
+                                        int& parity) {
+  if constexpr (TS == 0) team_sum<NV>(v, wpr, wave0, red, parity);
+  else group_sum<TS, NV>(v);
+}
+
 // ------------------------------------------------------------------------------------
 // Forward.
 // ------------------------------------------------------------------------------------
-template <int OP, int DX, int DW, int V, bool VEC>
+template <int OP, int DX, int DW, int V, bool VEC, int TS = 0>
 __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
   constexpr bool PF = fwd_prefetch(V, Ty<DX>::B);
@@ -105,7 +160,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
   using SX = typename Ty<DX>::S;
   __shared__ double red[2][16][4];
   int parity = 0;
-  const int T = p.team;
+  const int T = TS > 0 ? TS : p.team;
   const int tid = threadIdx.x;
   const int r = tid / T;
   const int t = tid - r * T;
@@ -116,7 +171,6 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
   const double inv_n = 1.0 / N;
   const double pad = static_cast<double>(T * V - N);  // zero-filled slots of the span
 
-  const uint32_t row_bytes = static_cast<uint32_t>(N) * Ty<DX>::B;
   const uint32_t par_bytes = static_cast<uint32_t>(N) * Ty<DW>::B;
 
   // Parameters of this thread's columns, loaded once per workgroup.  LayerNorm keeps w
@@ -145,20 +199,23 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
     FX res;
     double k;
   };
-  // rows are uniform per wave (teams are whole waves); rows past the workgroup's
-  // share get zero-byte resources: their loads read zeros and their stores vanish
-  auto row_of = [&](int it) {
-    return uniform((static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R + r);
+  // whole-wave teams: the row is uniform per wave; narrower teams: one row per lane group
+  auto row0_of = [&](int it) {
+    return uniform((static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R);
   };
-  auto rsrc = [&](const void* base, int64_t ld, int64_t row) {
-    return make_rsrc(static_cast<const SX*>(base) + row * ld, row < row_end ? row_bytes : 0u);
+  auto row_of = [&](int it) {
+    const int64_t row = (static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R + r;
+    if constexpr (TS == 0) return uniform(row);
+    else return row;
+  };
+  auto at = [&](const void* base, int64_t ld, int it) {
+    return row_at<SX, TS>(base, ld, row_of(it), row0_of(it), R, r, N, row_end);
   };
   auto load = [&](In& in, int it) {
-    const int64_t row = row_of(it);
-    const rsrc_t rx = rsrc(p.x, p.ldx, row);
-    in.x.load(rx, t, T);
-    if constexpr (OP == OP_FADD) in.res.load(rsrc(p.res, p.ldr, row), t, T);
-    if constexpr (OP == OP_LN) in.k = first_elem<DX>(rx);
+    const RowAt ax = at(p.x, p.ldx, it);
+    frag_load<TS>(in.x, ax, t, T, N);
+    if constexpr (OP == OP_FADD) frag_load<TS>(in.res, at(p.res, p.ldr, it), t, T, N);
+    if constexpr (OP == OP_LN) in.k = first_at<DX, TS>(ax);
   };
 
   auto process = [&](In& in, int it) {
@@ -176,7 +233,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
 #pragma unroll
       for (int i = 0; i < V; ++i) s[i] = xf.get(i) + in.res.get(i);
       xf.pack(s);  // residual_out = round(x + residual); the norm works on this value
-      xf.store_raw(rsrc(p.ro, p.ldro, row), t, T);
+      frag_store<TS>(xf, at(p.ro, p.ldro, it), t, T, N);
     }
     float o[V];
     if constexpr (OP == OP_RMS || OP == OP_FADD) {
@@ -186,7 +243,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
         const double v = static_cast<double>(xf.get(i));
         acc[0] = fma(v, v, acc[0]);
       }
-      team_sum<1>(acc, wpr, wave0, red, parity);
+      row_sum<TS, 1>(acc, wpr, wave0, red, parity);
       xf.opaque();
       const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
       const float rs = static_cast<float>(rstd);
@@ -202,7 +259,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
         acc[0] += d;
         acc[1] = fma(d, d, acc[1]);
       }
-      team_sum<2>(acc, wpr, wave0, red, parity);
+      row_sum<TS, 2>(acc, wpr, wave0, red, parity);
       xf.opaque();
       acc[0] = fma(pad, K, acc[0]);          // the zero-filled slots added -K each
       acc[1] = fma(-pad * K, K, acc[1]);     // ... and K^2 each to the squares
@@ -223,7 +280,7 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
     }
     FX yf;
     yf.pack(o);
-    yf.store_raw(rsrc(p.y, p.ldy, row), t, T);
+    frag_store<TS>(yf, at(p.y, p.ldy, it), t, T, N);
   };
 
   if constexpr (PF) {
@@ -328,20 +385,52 @@ __device__ __forceinline__ void combine_regs(const Acc<V, 0, S>& acc, float* dst
   }
 }
 
-// LDS accumulators (ACC = 1): every team takes part.  Team r handles the groups of four
-// elements j = r, r + R, ...; for each, thread t adds the R teams' float4 in team order
-// (16-byte reads of consecutive words) and writes the group's four columns with one
-// 16-byte store.  The caller has synchronised the workgroup after the last
-// accumulation.
+// LDS accumulators (ACC = 1): the R teams' float4 of each group j and thread slot t are
+// added in team order, in chunks of kCombineChunk teams when R is larger (sub-wave
+// teams): first every chunk is summed in order into its first team's slot, then the
+// chunk sums are added in order.  Either way a fixed order, independent of timing.
+// Every thread of the workgroup takes part; each output float4 is written as one
+// 16-byte store of four columns of the partial row `dst`.  The caller has synchronised
+// the workgroup after the last accumulation.
+constexpr int kCombineChunk = 8;
+
 template <int V, bool VEC, int EVE, int DX, int S>
-__device__ __forceinline__ void combine_lds(const float* block, float* dst, int r, int R, int t,
-                                            int T, int N) {
+__device__ __forceinline__ void combine_lds(float* block, float* dst, int R, int T, int N) {
   using FX = Frag<DX, V, EVE, VEC>;
-  const float4* b4 = reinterpret_cast<const float4*>(block);
-  for (int j = r; j < V / 4; j += R) {
+  constexpr int G = V / 4;
+  constexpr int C = kCombineChunk;
+  float4* b4 = reinterpret_cast<float4*>(block);
+  const int nth = blockDim.x;
+  const int tid = threadIdx.x;
+  int step = 1;
+  if (R > C) {
+    const int nch = (R + C - 1) / C;
+    for (int k = tid; k < G * T * nch; k += nth) {
+      const int ch = k % nch;
+      const int jt = k / nch;
+      const int t = jt % T;
+      const int j = jt / T;
+      float4* src = b4 + j * S + ch * C * T + t;
+      float4 a = src[0];
+      const int nq = min(C, R - ch * C);
+      for (int q = 1; q < nq; ++q) {
+        const float4 b = src[q * T];
+        a.x += b.x;
+        a.y += b.y;
+        a.z += b.z;
+        a.w += b.w;
+      }
+      src[0] = a;
+    }
+    __syncthreads();
+    step = C;
+  }
+  for (int k = tid; k < G * T; k += nth) {
+    const int t = k % T;
+    const int j = k / T;
     const float4* src = b4 + j * S + t;
     float4 a = src[0];
-    for (int q = 1; q < R; ++q) {
+    for (int q = step; q < R; q += step) {
       const float4 b = src[q * T];
       a.x += b.x;
       a.y += b.y;
@@ -356,9 +445,9 @@ __device__ __forceinline__ void combine_lds(const float* block, float* dst, int 
     } else {
       const float v[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int c = FX::col(4 * j + k, t, T);
-        if (c < N) dst[c] = v[k];
+      for (int q = 0; q < 4; ++q) {
+        const int c = FX::col(4 * j + q, t, T);
+        if (c < N) dst[c] = v[q];
       }
     }
   }
@@ -372,7 +461,8 @@ __device__ __forceinline__ void combine_lds(const float* block, float* dst, int 
 // XG: the weight is a 16-bit type and no offset is added, so g = dy * w is exact as an
 // fp32 product (at most 11 + 11 significant bits; exact unless it underflows fp32).
 // ------------------------------------------------------------------------------------
-template <int OP, int DX, int DW, int V, bool VEC, bool CDW, bool CDB, bool XG, int ACC>
+template <int OP, int DX, int DW, int V, bool VEC, bool CDW, bool CDB, bool XG, int ACC,
+          int TS = 0>
 __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
   constexpr int NG = (CDW ? 1 : 0) + (CDB ? 1 : 0);
@@ -386,7 +476,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   __shared__ double red[2][16][4];
   extern __shared__ float part[];
   int parity = 0;
-  const int T = p.team;
+  const int T = TS > 0 ? TS : p.team;
   const int tid = threadIdx.x;
   const int r = tid / T;
   const int t = tid - r * T;
@@ -398,7 +488,6 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   const double pad = static_cast<double>(T * V - N);
   const double off = (OP == OP_LN) ? 0.0 : static_cast<double>(p.offset);
 
-  const uint32_t row_bytes = static_cast<uint32_t>(N) * Ty<DX>::B;
   // The weight of this thread's columns.  Frozen instances keep it as loaded (16-bit
   // words unpacked on use: half the VGPRs of an fp32 copy, so more waves per SIMD); the
   // trainable ones, whose extra dW work makes them short of VALU issue rather than of
@@ -447,24 +536,28 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     FX d;   // fused add: dres_out
     double k;
   };
-  auto row_of = [&](int it) {
-    return uniform((static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R + r);
+  auto row0_of = [&](int it) {
+    return uniform((static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R);
   };
-  auto rsrc = [&](const void* base, int64_t ld, int64_t row) {
-    return make_rsrc(static_cast<const SX*>(base) + row * ld, row < row_end ? row_bytes : 0u);
+  auto row_of = [&](int it) {
+    const int64_t row = (static_cast<int64_t>(it) * gridDim.x + blockIdx.x) * R + r;
+    if constexpr (TS == 0) return uniform(row);
+    else return row;
+  };
+  auto at = [&](const void* base, int64_t ld, int it) {
+    return row_at<SX, TS>(base, ld, row_of(it), row0_of(it), R, r, N, row_end);
   };
   auto load = [&](In& in, int it) {
-    const int64_t row = row_of(it);
-    const rsrc_t rx = rsrc(p.x, p.ldx, row);
-    in.g.load(rsrc(p.dy, p.lddy, row), t, T);
-    in.x.load(rx, t, T);
+    const RowAt ax = at(p.x, p.ldx, it);
+    frag_load<TS>(in.g, at(p.dy, p.lddy, it), t, T, N);
+    frag_load<TS>(in.x, ax, t, T, N);
     if constexpr (OP == OP_FADD) {
       if (p.dres != nullptr)
-        in.d.load(rsrc(p.dres, p.lddr, row), t, T);
+        frag_load<TS>(in.d, at(p.dres, p.lddr, it), t, T, N);
       else
         in.d.zero();
     }
-    if constexpr (OP == OP_LN) in.k = first_elem<DX>(rx);
+    if constexpr (OP == OP_LN) in.k = first_at<DX, TS>(ax);
   };
 
   auto process = [&](In& in, int it) {
@@ -483,7 +576,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
         acc[0] = fma(xd, xd, acc[0]);
         acc[1] = fma(gd, xd, acc[1]);
       }
-      team_sum<2>(acc, wpr, wave0, red, parity);
+      row_sum<TS, 2>(acc, wpr, wave0, red, parity);
       xf.opaque();
       gf.opaque();
       wopaque(true);
@@ -521,7 +614,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
         acc[2] += g;
         acc[3] = fma(g, d, acc[3]);
       }
-      team_sum<4>(acc, wpr, wave0, red, parity);
+      row_sum<TS, 4>(acc, wpr, wave0, red, parity);
       xf.opaque();
       gf.opaque();
       wopaque(true);
@@ -558,7 +651,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     }
     FX of;
     of.pack(o);
-    of.store_raw(rsrc(p.dx, p.lddx, row), t, T);
+    frag_store<TS>(of, at(p.dx, p.lddx, it), t, T, N);
   };
 
   if constexpr (PF) {
@@ -586,8 +679,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   float* const dst_b = CDB ? p.pb + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
   if constexpr (NG > 0 && ACC == 1) {
     __syncthreads();  // every accumulation has landed
-    if constexpr (CDW) combine_lds<V, VEC, EVE, DX, S>(part, dst_w, r, R, t, T, N);
-    if constexpr (CDB) combine_lds<V, VEC, EVE, DX, S>(part + (CDW ? V * S : 0), dst_b, r, R, t, T, N);
+    if constexpr (CDW) combine_lds<V, VEC, EVE, DX, S>(part, dst_w, R, T, N);
+    if constexpr (CDB) combine_lds<V, VEC, EVE, DX, S>(part + (CDW ? V * S : 0), dst_b, R, T, N);
   } else {
     if constexpr (CDW) combine_regs<V, VEC, EVE, DX, S>(accw, dst_w, part, r, R, t, T, N);
     if constexpr (CDB) {

@@ -12,6 +12,7 @@ constexpr int kVs[] = {8, 16, 32, 48};
 struct Launch {
   int v;          // elements per thread per row (one of kVs)
   bool vec;       // 16-byte accesses (else element accesses)
+  int ts;         // 0: teams of whole waves; 8, 16, 32: sub-wave teams (V = 8, vec only)
   dim3 grid, block;
   size_t shmem;   // dynamic LDS bytes
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional kernel timing
@@ -50,6 +51,15 @@ bool launch_bwd_fadd(int dx, int dw, const BwdVariant& b, const Launch& l, const
 
 template <int OP, int DX, int DW>
 inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
+  if (l.ts != 0) {  // sub-wave teams: V = 8, 16-byte accesses
+    if (l.v != 8 || !l.vec) return false;
+    switch (l.ts) {
+      case 8: launch_kernel(fwd_kernel<OP, DX, DW, 8, true, 8>, l, s, a); return true;
+      case 16: launch_kernel(fwd_kernel<OP, DX, DW, 8, true, 16>, l, s, a); return true;
+      case 32: launch_kernel(fwd_kernel<OP, DX, DW, 8, true, 32>, l, s, a); return true;
+      default: return false;
+    }
+  }
 #define RN_CASE(V)                                                                       \
   case V:                                                                                \
     launch_kernel(l.vec ? fwd_kernel<OP, DX, DW, V, true> : fwd_kernel<OP, DX, DW, V, false>, \
@@ -59,20 +69,36 @@ inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
 #undef RN_CASE
 }
 
+template <typename K> inline bool bwd_go(K k, const Launch& l, const BwdArgs& a, hipStream_t s) {
+  if (l.shmem > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(l.shmem)) != hipSuccess)
+    return false;
+  launch_kernel(k, l, s, a);
+  return true;
+}
+
 template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, int ACC, int V>
 inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
   if constexpr (ACC == 0 && (CDW || CDB) && V < 48) {
     return false;  // up to V = 32 the LDS accumulator blocks always fit
   } else {
-    auto k = l.vec ? bwd_kernel<OP, DX, DW, V, true, CDW, CDB, XG, ACC>
-                   : bwd_kernel<OP, DX, DW, V, false, CDW, CDB, XG, ACC>;
-    if (l.shmem > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(l.shmem)) != hipSuccess)
-      return false;
-    launch_kernel(k, l, s, a);
-    return true;
+    if constexpr (V == 8 && (ACC == 1 || (!CDW && !CDB))) {
+      if (l.ts != 0) {  // sub-wave teams: V = 8, 16-byte accesses
+        if (!l.vec) return false;
+        switch (l.ts) {
+          case 8: return bwd_go(bwd_kernel<OP, DX, DW, 8, true, CDW, CDB, XG, ACC, 8>, l, a, s);
+          case 16: return bwd_go(bwd_kernel<OP, DX, DW, 8, true, CDW, CDB, XG, ACC, 16>, l, a, s);
+          case 32: return bwd_go(bwd_kernel<OP, DX, DW, 8, true, CDW, CDB, XG, ACC, 32>, l, a, s);
+          default: return false;
+        }
+      }
+    }
+    if (l.ts != 0) return false;
+    return bwd_go(l.vec ? bwd_kernel<OP, DX, DW, V, true, CDW, CDB, XG, ACC>
+                        : bwd_kernel<OP, DX, DW, V, false, CDW, CDB, XG, ACC>,
+                  l, a, s);
   }
 }
 

@@ -76,7 +76,20 @@ CONFIGS = [
     WIDE_128x18432_FP16,
     WIDE_128x18432_FP32,
 ]
-BY_NAME = {c.name: c for c in CONFIGS}
+# Narrow rows (a per-head norm over the head dimension: many rows of 64-256 elements).
+# Not among the five configurations; they measure the narrow-row path.
+QKNORM_65536x128 = Workload(
+    "rmsnorm_65536x128_bf16", "rmsnorm", 65536, 128, "bf16", "bf16", 1e-6, 0.0, "unit",
+    note="per-head RMSNorm over a 128-wide head dimension (4096 tokens x 16 heads)")
+QKNORM_32768x256 = Workload(
+    "rmsnorm_32768x256_bf16", "rmsnorm", 32768, 256, "bf16", "bf16", 1e-6, 0.0, "unit",
+    note="per-head RMSNorm over a 256-wide head dimension (4096 tokens x 8 heads)")
+NARROW_LN_65536x64 = Workload(
+    "layernorm_65536x64_bf16", "layernorm", 65536, 64, "bf16", "bf16", 1e-5, 0.0, "unit",
+    bias=True, note="LayerNorm over 64-wide rows")
+EXTRAS = [QKNORM_65536x128, QKNORM_32768x256, NARROW_LN_65536x64]
+
+BY_NAME = {c.name: c for c in CONFIGS + EXTRAS}
 
 
 def generate(wl: Workload, rows: slice | None = None) -> dict:
