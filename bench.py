@@ -341,7 +341,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"{wl.io} io, fp64 row statistics",
+        # arithmetic type: row statistics, LayerNorm outputs and dx are formed in fp64
+        # (storage type of the activations: config.io)
+        "dtype": "f64",
         "data": "synthetic (seeded CPU randn, no dataset)",
         "config": {"workload": wl.name, "op": wl.op, "M": wl.M, "N": wl.N, "io": wl.io,
                    "weight": wl.wt, "trainable_params": trainable,
