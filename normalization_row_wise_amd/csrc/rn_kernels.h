@@ -406,10 +406,10 @@ __device__ __forceinline__ void combine_lds(float* block, float* dst, int R, int
   if (R > C) {
     const int nch = (R + C - 1) / C;
     for (int k = tid; k < G * T * nch; k += nth) {
-      const int ch = k % nch;
-      const int jt = k / nch;
-      const int t = jt % T;
-      const int j = jt / T;
+      const int t = k % T;          // consecutive lanes: consecutive float4, no conflict
+      const int cj = k / T;
+      const int ch = cj % nch;
+      const int j = cj / nch;
       float4* src = b4 + j * S + ch * C * T + t;
       float4 a = src[0];
       const int nq = min(C, R - ch * C);
