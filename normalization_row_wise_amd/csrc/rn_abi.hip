@@ -140,16 +140,23 @@ inline int64_t team_of(int64_t N, int v) { return round_up(cdiv(N, v), 64); }
 inline int max_wg(int kind, int v, int eb) { return kind == 0 ? fwd_max_wg(v, eb) : bwd_max_wg(v, eb); }
 
 inline int pick_v(int kind, int op, int64_t N, int eb, int requested) {
-  if (requested) {
+  if (requested && (requested != 24 || kind == 2)) {  // V = 24: frozen backward only
     if (team_of(N, requested) <= max_wg(kind, requested, eb)) return requested;
   }
   const int pref = eb == 2 ? (op == OP_FADD ? 16 : 32) : 16;
   for (int v : kVs) {
     if (v > pref) break;
+    if (v == 24) continue;
     if (team_of(N, v) == 64) return v;                 // one wave covers the row
   }
-  for (int v : kVs) {
-    if (v < pref) continue;
+  // wide rows: the preferred V if its team fits, then V = 24 (16-wave workgroups) for
+  // the frozen backward (measured faster than V = 48 there: 18432-wide rows 9.3 -> 8.6
+  // us at 128 rows; slower in the forward, and not compiled with gradients), then 32 and
+  // 48
+  const int order[] = {pref, 24, 32, 48};
+  for (int v : order) {
+    if (v == 24 && kind != 2) continue;
+    if (v != 24 && v < pref) continue;
     if (team_of(N, v) <= max_wg(kind, v, eb)) return v;
   }
   return 0;

@@ -17,15 +17,17 @@
 // error that the cancellation in g - xhat * mean(g * xhat) turns into whole-ulp
 // errors of small dx values.  RMSNorm y (no cancellation) is formed in fp32.
 //
-// Work layout.  A team of T = 64 * W threads owns one row at a time (rn_device.h);
-// a workgroup holds R teams and makes rows_per_wg / R passes.  Pass `it` of workgroup
-// `b` takes rows (it * grid + b) * R .. + R - 1 (grid-stride): the rows in flight
-// across the chip at any moment form one contiguous window of the tensor, instead of
-// one slice per workgroup scattered over all of it (measured faster at large M).
-// When a thread's share of a row is at most 64 bytes per tensor, the next row's
-// tensors are loaded into a second register set before the current row is reduced
-// (two rows in flight per team).  Columns past N inside the team's span are loaded
-// as zeros; LayerNorm's shifted sums are corrected for them once per row.
+// Work layout.  A team of T threads owns one row at a time (rn_device.h): T = 64 * W
+// (whole waves), or T = TS = 8, 16 or 32 lanes for rows of at most 256 elements
+// (several rows per wave).  A workgroup holds R teams and makes rows_per_wg / R
+// passes.  Pass `it` of workgroup `b` takes rows (it * grid + b) * R .. + R - 1
+// (grid-stride): the rows in flight across the chip at any moment form one contiguous
+// window of the tensor, instead of one slice per workgroup scattered over all of it
+// (measured faster at large M).  When a thread's share of the row tensors is small
+// enough (fwd_prefetch, bwd_prefetch), the next row's tensors are loaded into a second
+// register set before the current row is reduced (two rows in flight per team).
+// Columns past N inside the team's span are loaded as zeros; LayerNorm's shifted sums
+// are corrected for them once per row.
 #pragma once
 #include "rn_device.h"
 
@@ -81,9 +83,16 @@ constexpr bool bwd_prefetch(int V, int B, bool grads, int nin) {
   return lane_bytes(V, B) * nin <= 2 * (grads ? RN_BWD_PF_BYTES : RN_FROZEN_PF_BYTES);
 }
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
-// (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.
-constexpr int fwd_max_wg(int V, int B) { return lane_bytes(V, B) <= RN_FWD_BIG_WG_BYTES ? 1024 : 512; }
-constexpr int bwd_max_wg(int V, int B) { return lane_bytes(V, B) <= RN_BWD_BIG_WG_BYTES ? 1024 : 512; }
+// (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.  V = 24
+// exists for the frozen backward of wide rows (up to 1024 * 24 = 24576 elements) and
+// always takes 16 waves: twelve 64-lane waves per row of 18432 halve each lane's serial
+// work against V = 48.
+constexpr int fwd_max_wg(int V, int B) {
+  return (V == 24 || lane_bytes(V, B) <= RN_FWD_BIG_WG_BYTES) ? 1024 : 512;
+}
+constexpr int bwd_max_wg(int V, int B) {
+  return (V == 24 || lane_bytes(V, B) <= RN_BWD_BIG_WG_BYTES) ? 1024 : 512;
+}
 
 // The row's first element (0 for a zero-byte resource).
 template <int DX> __device__ __forceinline__ double first_elem(rsrc_t rs) {

@@ -6,8 +6,9 @@
 
 namespace rn {
 
-// Elements per thread per row that are compiled (for every type and both access modes).
-constexpr int kVs[] = {8, 16, 32, 48};
+// Elements per thread per row that are compiled (for every type and both access modes;
+// V = 24 for the frozen backward only).
+constexpr int kVs[] = {8, 16, 24, 32, 48};
 
 struct Launch {
   int v;          // elements per thread per row (one of kVs)
@@ -65,7 +66,10 @@ inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
     launch_kernel(l.vec ? fwd_kernel<OP, DX, DW, V, true> : fwd_kernel<OP, DX, DW, V, false>, \
                   l, s, a);                                                              \
     return true;
-  switch (l.v) { RN_CASE(8) RN_CASE(16) RN_CASE(32) RN_CASE(48) default: return false; }
+  switch (l.v) {
+    RN_CASE(8) RN_CASE(16) RN_CASE(32) RN_CASE(48)
+    default: return false;
+  }
 #undef RN_CASE
 }
 
@@ -81,8 +85,10 @@ template <typename K> inline bool bwd_go(K k, const Launch& l, const BwdArgs& a,
 
 template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, int ACC, int V>
 inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
-  if constexpr (ACC == 0 && (CDW || CDB) && V < 48) {
-    return false;  // up to V = 32 the LDS accumulator blocks always fit
+  if constexpr ((ACC == 0 && (CDW || CDB) && V < 48) || (V == 24 && (CDW || CDB))) {
+    // up to V = 32 the LDS accumulator blocks always fit; V = 24 (16 waves, 128 VGPRs)
+    // is compiled for the frozen backward only (with gradients it would spill)
+    return false;
   } else {
     if constexpr (V == 8 && (ACC == 1 || (!CDW && !CDB))) {
       if (l.ts != 0) {  // sub-wave teams: V = 8, 16-byte accesses
@@ -107,6 +113,7 @@ inline bool bwd_v(const Launch& l, const BwdArgs& a, hipStream_t s) {
   switch (l.v) {
     case 8: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 8>(l, a, s);
     case 16: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 16>(l, a, s);
+    case 24: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 24>(l, a, s);
     case 32: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 32>(l, a, s);
     case 48: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 48>(l, a, s);
     default: return false;
