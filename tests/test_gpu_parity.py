@@ -268,3 +268,30 @@ def test_single_workgroup_gradient_direct_and_via_workspace(op, m):
         assert torch.equal(a, b), k
         assert gp.f32_report(a.cpu(), ref[k]) <= gp.REL_GRAD, k
     assert torch.all(buf[0] == 7.0) and torch.all(buf[1 + N:N + 5] == 7.0)
+
+
+# ---- the accuracy comparison of the Gemma page, on the GPU path -------------------------
+
+def test_gemma_fused_offset_accuracy_against_preadd_control():
+    # "fix(cutedsl): fuse Gemma RMSNorm weight offset in FP32", PyTorch accuracy
+    # comparison: pre-adding the offset to the bf16 weight costs ~3e-3 relative L2 in y;
+    # adding it in fp32 inside the kernel brings y to the bf16 rounding floor.
+    import normalization_row_wise_amd as rn
+    from tests.golden import load
+    g = load("accuracy_magnitudes.txt")
+    wl = workloads.GEMMA_RMS_128x4096
+    _say("gemma accuracy", wl.name)
+    t = workloads.generate(wl)
+    d = gp.to_device(t)
+    fused, _ = rn.rmsnorm_fwd(d["x"], d["w"], t["eps"], t["offset"])
+    w_pre = (t["w"].double() + t["offset"]).to(torch.bfloat16).to(gp.dev())   # bf16(w + 1)
+    preadd, _ = rn.rmsnorm_fwd(d["x"], w_pre, t["eps"], 0.0)
+    torch.cuda.synchronize()
+    ref, _ = oracle.rmsnorm_fwd(workloads.as_f64(t["x"]), workloads.as_f64(t["w"]), t["eps"],
+                                t["offset"])
+    r16 = oracle.round_to(ref, "bf16")
+    e_fused = gp.rel_l2(oracle.from_bits(gp.gpu_bits(fused.cpu(), "bf16"), "bf16"), r16)
+    e_pre = gp.rel_l2(oracle.from_bits(gp.gpu_bits(preadd.cpu(), "bf16"), "bf16"), r16)
+    assert e_fused <= 1e-4, e_fused
+    assert g["rmsnorm_y_before"] / 3 <= e_pre <= g["rmsnorm_y_before"] * 3, e_pre
+    assert e_pre > 30 * e_fused
