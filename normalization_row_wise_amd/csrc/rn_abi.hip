@@ -130,9 +130,10 @@ inline bool vec_ok(const void* p, int64_t ld, int64_t M, int eb) {
 }
 
 // Elements per thread per row.  Preferred: 64 bytes of each row tensor per lane (32
-// elements of a 16-bit type, 16 of fp32); the fused add moves more row tensors per
-// element and prefers 16 elements of a 16-bit type (its backward then fits the
-// next-row prefetch; measured faster in all three kernels at 2048 x 8192 bf16).
+// elements of a 16-bit type, 16 of fp32); the fused add's forward and trainable
+// backward move more row tensors per element and prefer 16 elements of a 16-bit type
+// (the backward then fits the next-row prefetch; measured faster at 2048 x 8192 bf16),
+// its frozen backward keeps 32 (26.4 us against 27.4 there).
 // Narrow rows use the smallest V that still covers the row with one wave; wide rows
 // move up to a larger V when the team would exceed the kernel's workgroup limit.
 inline int64_t team_of(int64_t N, int v) { return round_up(cdiv(N, v), 64); }
@@ -143,7 +144,7 @@ inline int pick_v(int kind, int op, int64_t N, int eb, int requested) {
   if (requested && (requested != 24 || kind == 2)) {  // V = 24: frozen backward only
     if (team_of(N, requested) <= max_wg(kind, requested, eb)) return requested;
   }
-  const int pref = eb == 2 ? (op == OP_FADD ? 16 : 32) : 16;
+  const int pref = eb == 2 ? (op == OP_FADD && kind != 2 ? 16 : 32) : 16;
   for (int v : kVs) {
     if (v > pref) break;
     if (v == 24) continue;
