@@ -42,8 +42,14 @@
  *   - Errors: arguments are checked before any HIP call; on error nothing is enqueued
  *     and an rn_status < 0 is returned.  RN_ERR_HIP reports a failed launch.
  *   - Aliasing: an output may alias an input of the same shape and stride (y == x,
- *     residual_out == residual, dx == dy or dx == dres_out: each element is read
- *     before it is written by the same thread).  Any other overlap is undefined.
+ *     residual_out == residual, dx == dy or dx == dres_out): such calls run kernels
+ *     in which each element is read before it is written by the same thread (never
+ *     the split-row kernels, whose workgroups read the whole row).  Any other overlap
+ *     is undefined.
+ *   - Few long rows (aligned rows of at least two spans of 256 16-byte accesses, rows
+ *     x spans <= 64 in the forward and <= 256 in the backward) are spread over several
+ *     workgroups each; the results meet the same accuracy contract, and dx does not
+ *     depend on which parameter gradients are requested.
  */
 #ifndef ROWNORM_H
 #define ROWNORM_H
@@ -75,9 +81,10 @@ typedef enum rn_status {
  * parameter gradients at this shape: per-workgroup partial rows of dw / db,
  * reduced by a second kernel in fixed order.  0 when n_param_grads == 0 (frozen
  * parameters need no workspace: [frozen], Motivation).  Returns 0 for invalid shapes.
- * When a single workgroup covers every row (very small M) and dw / db are 16-byte
- * aligned, the gradients are written directly and the workspace is left untouched;
- * it must still be passed. */
+ * When the call has a single partial row (very small M: one workgroup covering every
+ * row, or one row spread over workgroups) and dw / db are 16-byte aligned, the
+ * gradients are written directly and the workspace is left untouched; it must still
+ * be passed. */
 size_t rn_bwd_workspace_bytes(int64_t M, int64_t N, int n_param_grads);
 
 /* RMSNorm forward.  [gemma] Summary: offset added to the weight in fp32 in-kernel.

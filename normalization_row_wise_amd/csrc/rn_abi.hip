@@ -130,35 +130,26 @@ inline bool vec_ok(const void* p, int64_t ld, int64_t M, int eb) {
 }
 
 // Elements per thread per row.  Preferred: 64 bytes of each row tensor per lane (32
-// elements of a 16-bit type, 16 of fp32); the fused add's forward and trainable
-// backward move more row tensors per element and prefer 16 elements of a 16-bit type
-// (the backward then fits the next-row prefetch; measured faster at 2048 x 8192 bf16),
-// its frozen backward keeps 32 (26.4 us against 27.4 there).
-// Narrow rows use the smallest V that still covers the row with one wave; wide rows
-// move up to a larger V when the team would exceed the kernel's workgroup limit.
+// elements of a 16-bit type, 16 of fp32); the fused add moves more row tensors per
+// element and prefers 16 elements of a 16-bit type (its backward then fits the next-row
+// prefetch; measured faster at 2048 x 8192 bf16).  Narrow rows use the smallest V that
+// still covers the row with one wave; wide rows move up to a larger V when the team
+// would exceed the kernel's workgroup limit.  The choice never depends on which
+// parameter gradients a backward computes: frozen and trainable calls lay the row out
+// alike, add its sums in the same order and so give bit-identical dx.
 inline int64_t team_of(int64_t N, int v) { return round_up(cdiv(N, v), 64); }
 
 inline int max_wg(int kind, int v, int eb) { return kind == 0 ? fwd_max_wg(v, eb) : bwd_max_wg(v, eb); }
 
 inline int pick_v(int kind, int op, int64_t N, int eb, int requested) {
-  if (requested && (requested != 24 || kind == 2)) {  // V = 24: frozen backward only
-    if (team_of(N, requested) <= max_wg(kind, requested, eb)) return requested;
-  }
-  const int pref = eb == 2 ? (op == OP_FADD && kind != 2 ? 16 : 32) : 16;
+  if (requested && team_of(N, requested) <= max_wg(kind, requested, eb)) return requested;
+  const int pref = eb == 2 ? (op == OP_FADD ? 16 : 32) : 16;
   for (int v : kVs) {
     if (v > pref) break;
-    if (v == 24) continue;
-    if (team_of(N, v) == 64) return v;                 // one wave covers the row
+    if (team_of(N, v) == 64) return v;  // one wave covers the row
   }
-  // wide rows: the preferred V if its team fits, then V = 24 (16-wave workgroups) for
-  // the frozen backward (measured faster than V = 48 there: 18432-wide rows 9.3 -> 8.6
-  // us at 128 rows; slower in the forward, and not compiled with gradients), then 32 and
-  // 48
-  const int order[] = {pref, 24, 32, 48};
-  for (int v : order) {
-    if (v == 24 && kind != 2) continue;
-    if (v != 24 && v < pref) continue;
-    if (team_of(N, v) <= max_wg(kind, v, eb)) return v;
+  for (int v : kVs) {
+    if (v >= pref && team_of(N, v) <= max_wg(kind, v, eb)) return v;
   }
   return 0;
 }
@@ -274,6 +265,32 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
   return s;
 }
 
+// Split rows (rn_split.h): each row spread over workgroups of SPLIT_WG threads, one per
+// 16-byte-access span of the row, when the rows are too few to keep the CUs busy one
+// team each (a decode row, a small batch).  Every workgroup walks its whole row for the
+// statistics, so a row takes at least two spans, and all rows' spans together stay
+// within one workgroup per CU.  The backward takes the same decision with and without
+// parameter gradients, so dx comes from the same kernel and the same sums either way;
+// its row kernels with gradients are slow at small M (few partial rows), hence the
+// wider bound.  The forward's redundant statistics cost more than they save beyond a
+// quarter of the CUs (measured: 28 rows of 18432 bf16, 4.8 us split against 4.2).
+// Needs 16-byte accesses and no output that is also an input; not taken while a
+// launch-shape override is set for the kind.  0: not split.
+#ifndef RN_SPLIT_MAX_WG_FWD
+#define RN_SPLIT_MAX_WG_FWD 64
+#endif
+#ifndef RN_SPLIT_MAX_WG_BWD
+#define RN_SPLIT_MAX_WG_BWD 256
+#endif
+inline int64_t split_spans(int kind, int64_t M, int64_t N, int eb, bool vec, bool aliased) {
+  const Override& o = g_override[kind];
+  if (!vec || aliased || o.v || o.rows || o.wg_rows) return 0;
+  const int64_t spans = cdiv(N, static_cast<int64_t>(SPLIT_WG) * (16 / eb));
+  const int64_t cap = kind == 0 ? RN_SPLIT_MAX_WG_FWD : RN_SPLIT_MAX_WG_BWD;
+  if (spans < 2 || M * spans > cap) return 0;
+  return spans;
+}
+
 inline int launched() { return hipGetLastError() == hipSuccess ? RN_OK : RN_ERR_HIP; }
 
 int colsum(const float* ws, int64_t ldws, int P, int64_t N, float* o0, float* o1,
@@ -355,6 +372,8 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
 
   int64_t max_ld = std::max(ldx, ldy);
   if (op == OP_FADD) max_ld = std::max({max_ld, ldr, ldro});
+  const bool aliased = y == x || (op == OP_FADD && (y == res || ro == x || ro == res));
+  const int64_t spans = split_spans(0, M, N, eb, vec, aliased);
   const Shape s = plan(0, op, M, N, xt, 0, vec, M > 1 ? max_ld : N);
   FwdArgs a{};
   a.x = x; a.ldx = ldx; a.res = res; a.ldr = ldr; a.w = w; a.b = b;
@@ -364,6 +383,11 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   a.eps = eps; a.offset = offset;
   Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
            dim3(static_cast<unsigned>(s.R * s.team)), 0, g_timing[0][0], g_timing[0][1]};
+  if (spans > 0) {
+    l.split = true;
+    l.grid = dim3(static_cast<unsigned>(spans), static_cast<unsigned>(M));
+    l.block = dim3(SPLIT_WG);
+  }
   bool ok = false;
   const int dx = to_dt(xt), dw = to_dt(wt);
   if (op == OP_RMS) ok = launch_fwd_rms(dx, dw, l, a, st);
@@ -427,23 +451,34 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
 
   int64_t max_ld = std::max({lddy, ldx, lddx});
   if (dres != nullptr) max_ld = std::max(max_ld, lddr);
-  const Shape s = plan(ngrads > 0 ? 1 : 2, op, M, N, xt, ngrads, vec, M > 1 ? max_ld : N);
+  const int kind = ngrads > 0 ? 1 : 2;
+  const bool aliased = dx == dy || dx == x || (dres != nullptr && dx == dres);
+  const int64_t spans = split_spans(kind, M, N, eb, vec, aliased);
+  const Shape s = plan(kind, op, M, N, xt, ngrads, vec, M > 1 ? max_ld : N);
+  // partial rows: one per workgroup, or one per row when rows are split
+  const int P = spans > 0 ? static_cast<int>(M) : s.P;
   BwdArgs a{};
   a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
   a.dx = dx; a.lddx = lddx;
-  // One workgroup covering every row (a decode row, say): its combined row is the
-  // gradient itself, written in place of a partial row, and no column sum is launched.
-  // The kernel writes 16-byte groups, so this needs 16-byte aligned outputs.
-  const bool direct = s.P == 1 && aligned16(dw) && aligned16(db);
+  // One partial row in all (a decode row, say): it is the gradient itself, written in
+  // place of a partial row, and no column sum is launched.  The kernels write 16-byte
+  // groups, so this needs 16-byte aligned outputs.
+  const bool direct = P == 1 && aligned16(dw) && aligned16(db);
   float* const part = static_cast<float*>(ws);
   a.pw = direct ? dw : part;
-  a.pb = direct ? db : part + (dw != nullptr ? static_cast<int64_t>(s.P) * ldws : 0);
+  a.pb = direct ? db : part + (dw != nullptr ? static_cast<int64_t>(P) * ldws : 0);
   a.ldws = ldws;
   a.M = M; a.N = static_cast<int>(N); a.team = s.team;
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
   Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
            dim3(static_cast<unsigned>(s.R * s.team)), s.shmem, g_timing[1][0], g_timing[1][1]};
+  if (spans > 0) {
+    l.split = true;
+    l.grid = dim3(static_cast<unsigned>(spans), static_cast<unsigned>(M));
+    l.block = dim3(SPLIT_WG);
+    l.shmem = 0;
+  }
   bool ok = false;
   const int dxt = to_dt(xt), dwt = to_dt(wt);
   // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it
@@ -455,7 +490,7 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   if (!ok) return RN_ERR_DTYPE;
   if ((e = launched()) != RN_OK) return e;
   if (ngrads == 0 || direct) return RN_OK;  // frozen, or the gradient written directly
-  return colsum(static_cast<const float*>(ws), ldws, s.P, N, dw, db, st);
+  return colsum(static_cast<const float*>(ws), ldws, P, N, dw, db, st);
 }
 
 int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, void* dx,

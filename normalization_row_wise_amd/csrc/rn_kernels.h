@@ -83,15 +83,12 @@ constexpr bool bwd_prefetch(int V, int B, bool grads, int nin) {
   return lane_bytes(V, B) * nin <= 2 * (grads ? RN_BWD_PF_BYTES : RN_FROZEN_PF_BYTES);
 }
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
-// (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.  V = 24
-// exists for the frozen backward of wide rows (up to 1024 * 24 = 24576 elements) and
-// always takes 16 waves: twelve 64-lane waves per row of 18432 halve each lane's serial
-// work against V = 48.
+// (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.
 constexpr int fwd_max_wg(int V, int B) {
-  return (V == 24 || lane_bytes(V, B) <= RN_FWD_BIG_WG_BYTES) ? 1024 : 512;
+  return lane_bytes(V, B) <= RN_FWD_BIG_WG_BYTES ? 1024 : 512;
 }
 constexpr int bwd_max_wg(int V, int B) {
-  return (V == 24 || lane_bytes(V, B) <= RN_BWD_BIG_WG_BYTES) ? 1024 : 512;
+  return lane_bytes(V, B) <= RN_BWD_BIG_WG_BYTES ? 1024 : 512;
 }
 
 // The row's first element (0 for a zero-byte resource).
@@ -502,6 +499,14 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   // trainable ones, whose extra dW work makes them short of VALU issue rather than of
   // waves, keep an fp32 copy and save the unpacking.
   constexpr bool PACKW = NG == 0;
+  // The same budget argument for the row itself: a trainable launch of whole-wave
+  // teams has at most one workgroup per CU (one partial row each, at most 256 of them),
+  // so it can keep what the statistics pass derived from dy (V <= 32) and x (V <= 16)
+  // alive for the output pass instead of unpacking and converting again (measured:
+  // fused add 2048 x 8192 bf16 34.8 -> 33.4 us, LayerNorm 2048 x 4096 bf16 19.4 ->
+  // 18.7 us).  Wider rows and the element-access instances would spill.
+  constexpr bool KEEP_G = NG > 0 && VEC && TS == 0 && V <= 32;
+  constexpr bool KEEP_X = NG > 0 && VEC && TS == 0 && V <= 16;
   FW wf;
   float wv[PACKW ? 1 : V];
   wf.load(make_rsrc(p.w, static_cast<uint32_t>(N) * Ty<DW>::B), t, T);
@@ -586,8 +591,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
         acc[1] = fma(gd, xd, acc[1]);
       }
       row_sum<TS, 2>(acc, wpr, wave0, red, parity);
-      xf.opaque();
-      gf.opaque();
+      if constexpr (!KEEP_X) xf.opaque();
+      if constexpr (!KEEP_G) gf.opaque();
       wopaque(true);
       const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
       // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
@@ -624,8 +629,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
         acc[3] = fma(g, d, acc[3]);
       }
       row_sum<TS, 4>(acc, wpr, wave0, red, parity);
-      xf.opaque();
-      gf.opaque();
+      if constexpr (!KEEP_X) xf.opaque();
+      if constexpr (!KEEP_G) gf.opaque();
       wopaque(true);
       acc[0] = fma(pad, K, acc[0]);          // zero-filled slots: d = -K, g = 0
       acc[1] = fma(-pad * K, K, acc[1]);

@@ -2,13 +2,12 @@
 #pragma once
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
-#include "rn_kernels.h"
+#include "rn_split.h"
 
 namespace rn {
 
-// Elements per thread per row that are compiled (for every type and both access modes;
-// V = 24 for the frozen backward only).
-constexpr int kVs[] = {8, 16, 24, 32, 48};
+// Elements per thread per row that are compiled (for every type and both access modes).
+constexpr int kVs[] = {8, 16, 32, 48};
 
 struct Launch {
   int v;          // elements per thread per row (one of kVs)
@@ -17,6 +16,7 @@ struct Launch {
   dim3 grid, block;
   size_t shmem;   // dynamic LDS bytes
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional kernel timing
+  bool split = false;  // rows spread over workgroups (rn_split.h; v, ts unused)
 };
 
 // Launch through hipExtLaunchKernel when timing events are attached.
@@ -52,6 +52,11 @@ bool launch_bwd_fadd(int dx, int dw, const BwdVariant& b, const Launch& l, const
 
 template <int OP, int DX, int DW>
 inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
+  if (l.split) {
+    if (!l.vec) return false;
+    launch_kernel(split_fwd_kernel<OP, DX, DW>, l, s, a);
+    return true;
+  }
   if (l.ts != 0) {  // sub-wave teams: V = 8, 16-byte accesses
     if (l.v != 8 || !l.vec) return false;
     switch (l.ts) {
@@ -85,9 +90,8 @@ template <typename K> inline bool bwd_go(K k, const Launch& l, const BwdArgs& a,
 
 template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, int ACC, int V>
 inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
-  if constexpr ((ACC == 0 && (CDW || CDB) && V < 48) || (V == 24 && (CDW || CDB))) {
-    // up to V = 32 the LDS accumulator blocks always fit; V = 24 (16 waves, 128 VGPRs)
-    // is compiled for the frozen backward only (with gradients it would spill)
+  if constexpr (ACC == 0 && (CDW || CDB) && V < 48) {
+    // up to V = 32 the LDS accumulator blocks always fit
     return false;
   } else {
     if constexpr (V == 8 && (ACC == 1 || (!CDW && !CDB))) {
@@ -113,7 +117,6 @@ inline bool bwd_v(const Launch& l, const BwdArgs& a, hipStream_t s) {
   switch (l.v) {
     case 8: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 8>(l, a, s);
     case 16: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 16>(l, a, s);
-    case 24: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 24>(l, a, s);
     case 32: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 32>(l, a, s);
     case 48: return bwd_one<OP, DX, DW, CDW, CDB, XG, ACC, 48>(l, a, s);
     default: return false;
@@ -124,6 +127,17 @@ inline bool bwd_v(const Launch& l, const BwdArgs& a, hipStream_t s) {
 template <int OP, int DX, int DW, bool CDW, bool CDB>
 inline bool bwd_flags(const BwdVariant& b, const Launch& l, const BwdArgs& a, hipStream_t s) {
   constexpr bool can_xg = Ty<DW>::B == 2;
+  if (l.split) {
+    if (!l.vec) return false;
+    if constexpr (can_xg) {
+      if (b.xg) {
+        launch_kernel(split_bwd_kernel<OP, DX, DW, CDW, CDB, true>, l, s, a);
+        return true;
+      }
+    }
+    launch_kernel(split_bwd_kernel<OP, DX, DW, CDW, CDB, false>, l, s, a);
+    return true;
+  }
   if constexpr (!CDW && !CDB) {
     if constexpr (can_xg) {
       if (b.xg) return bwd_v<OP, DX, DW, false, false, true, 0>(l, a, s);

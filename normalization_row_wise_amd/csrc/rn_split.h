@@ -1,0 +1,290 @@
+// rn_split.h — kernels for a few long rows (a decode step, a small batch): each row is
+// spread over several workgroups.
+//
+// With one team per row, a single row of 18432 elements is the serial work of one CU
+// (its fp64 passes alone take a few microseconds of that CU's vector ALUs) while the
+// other CUs idle.  Here workgroup (c, i) of SPLIT_WG threads owns span c of row i: the
+// columns of lane t's 16-byte access c * SPLIT_WG + t.  It first walks the whole row
+// and forms the row's sums itself, in the same order as every other workgroup of the
+// row, so all of them hold bitwise-identical statistics and none waits for another
+// (the redundant reads hit L2); then it writes its own span of the outputs.  The
+// arithmetic is the one of the row kernels (rn_kernels.h): fp64 sums, LayerNorm y and
+// every dx formed in fp64 and rounded once, RMSNorm y in fp32 with the offset added to
+// the weight in fp32 ([gemma], Summary).
+//
+// Parameter gradients: row i's products dy * xhat (and dy) for the span are written to
+// partial row i, so the partial rows are the rows themselves (P = M) and the column
+// sum adds them; a single row writes dw / db directly.
+//
+// Requirements (checked by the caller): 16-byte accesses (aligned rows, N a multiple
+// of 16 / sizeof(element)), and no output that is also an input: another workgroup of
+// the row may still be reading it.
+#pragma once
+#include "rn_kernels.h"
+
+namespace rn {
+
+#ifndef RN_SPLIT_U
+#define RN_SPLIT_U 4
+#endif
+constexpr int SPLIT_WG = 256;         // threads per workgroup
+constexpr int SPLIT_U = RN_SPLIT_U;   // spans a lane has in flight during the statistics walk
+
+// Buffer resource over row `row` of a row tensor (N elements of SX).
+template <typename SX>
+__device__ __forceinline__ rsrc_t row_rsrc(const void* base, int64_t ld, int64_t row, int N) {
+  return make_rsrc(static_cast<const SX*>(base) + row * ld, static_cast<uint32_t>(N) * sizeof(SX));
+}
+
+// Forward.  grid = (spans per row, M).
+template <int OP, int DX, int DW>
+__global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
+  constexpr int EVE = 16 / Ty<DX>::B;
+  using FX = Frag<DX, EVE, EVE, true>;
+  using FW = Frag<DW, EVE, EVE, true>;
+  using SX = typename Ty<DX>::S;
+  using SW = typename Ty<DW>::S;
+  __shared__ double red[2][16][4];
+  int parity = 0;
+  const int t = threadIdx.x;
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int N = p.N;
+  const int NS = gridDim.x;
+  const double inv_n = 1.0 / N;
+  const double pad = static_cast<double>(NS) * SPLIT_WG * EVE - N;
+
+  const rsrc_t rx = row_rsrc<SX>(p.x, p.ldx, row, N);
+  rsrc_t rr = rx;
+  if constexpr (OP == OP_FADD) rr = row_rsrc<SX>(p.res, p.ldr, row, N);
+  // this workgroup's span: inputs and parameters, loaded first
+  const int a0 = c * SPLIT_WG + t;
+  FX ox, orr;
+  FW ow, ob;
+  ox.load(rx, a0, 0);
+  if constexpr (OP == OP_FADD) orr.load(rr, a0, 0);
+  const uint32_t par_bytes = static_cast<uint32_t>(N) * sizeof(SW);
+  ow.load(make_rsrc(p.w, par_bytes), a0, 0);
+  if constexpr (OP == OP_LN) {
+    if (p.b != nullptr) ob.load(make_rsrc(p.b, par_bytes), a0, 0);
+    else ob.zero();
+  }
+  const double K = OP == OP_LN ? first_elem<DX>(rx) : 0.0;
+
+  // FusedAdd: the norm works on round(x + residual)
+  auto summed = [&](FX& f, const FX& r) {
+    if constexpr (OP == OP_FADD) {
+      float s[EVE];
+#pragma unroll
+      for (int i = 0; i < EVE; ++i) s[i] = f.get(i) + r.get(i);
+      f.pack(s);
+    }
+  };
+
+  // statistics of the whole row: RMS sum x^2; LN sum d, sum d^2 with d = x - K
+  double acc[2] = {0.0, 0.0};
+  for (int s0 = 0; s0 < NS; s0 += SPLIT_U) {
+    FX xs[SPLIT_U], rs[SPLIT_U];
+#pragma unroll
+    for (int u = 0; u < SPLIT_U; ++u) {
+      xs[u].load(rx, (s0 + u) * SPLIT_WG + t, 0);
+      if constexpr (OP == OP_FADD) rs[u].load(rr, (s0 + u) * SPLIT_WG + t, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < SPLIT_U; ++u) {
+      if (s0 + u >= NS) break;  // uniform
+      summed(xs[u], rs[u]);
+#pragma unroll
+      for (int i = 0; i < EVE; ++i) {
+        if constexpr (OP == OP_LN) {
+          const double d = static_cast<double>(xs[u].get(i)) - K;
+          acc[0] += d;
+          acc[1] = fma(d, d, acc[1]);
+        } else {
+          const double v = static_cast<double>(xs[u].get(i));
+          acc[0] = fma(v, v, acc[0]);
+        }
+      }
+    }
+  }
+  team_sum<2>(acc, SPLIT_WG / 64, 0, red, parity);
+
+  summed(ox, orr);
+  if constexpr (OP == OP_FADD) ox.store_raw(row_rsrc<SX>(p.ro, p.ldro, row, N), a0, 0);
+  float o[EVE];
+  if constexpr (OP == OP_LN) {
+    acc[0] = fma(pad, K, acc[0]);  // slots past N read as zero: d = -K each
+    acc[1] = fma(-pad * K, K, acc[1]);
+    const double delta = acc[0] * inv_n;
+    const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
+    const double rstd = rsqrt_d(var + static_cast<double>(p.eps));
+    const double mean = K + delta;
+#pragma unroll
+    for (int i = 0; i < EVE; ++i) {
+      const double e = static_cast<double>(ox.get(i)) - mean;
+      o[i] = static_cast<float>(
+          fma(e * rstd, static_cast<double>(ow.get(i)), static_cast<double>(ob.get(i))));
+    }
+    if (c == 0 && t == 0) {
+      if (p.rstd != nullptr) p.rstd[row] = static_cast<float>(rstd);
+      if (p.mean != nullptr) p.mean[row] = static_cast<float>(mean);
+    }
+  } else {
+    const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+    const float rs = static_cast<float>(rstd);
+#pragma unroll
+    for (int i = 0; i < EVE; ++i) o[i] = (ox.get(i) * rs) * (ow.get(i) + p.offset);
+    if (c == 0 && t == 0 && p.rstd != nullptr) p.rstd[row] = rs;
+  }
+  FX yf;
+  yf.pack(o);
+  yf.store_raw(row_rsrc<SX>(p.y, p.ldy, row, N), a0, 0);
+}
+
+// Backward (stage 1).  grid = (spans per row, M).  pw / pb: row i of the partial rows
+// (stride ldws), or dw / db themselves when M = 1.
+template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG>
+__global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
+  constexpr int EVE = 16 / Ty<DX>::B;
+  using FX = Frag<DX, EVE, EVE, true>;
+  using FW = Frag<DW, EVE, EVE, true>;
+  using SX = typename Ty<DX>::S;
+  using SW = typename Ty<DW>::S;
+  static_assert(!(CDB && OP != OP_LN), "only LayerNorm has a bias");
+  static_assert(!(XG && Ty<DW>::B != 2), "exact fp32 products need a 16-bit weight");
+  __shared__ double red[2][16][4];
+  int parity = 0;
+  const int t = threadIdx.x;
+  const int c = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int N = p.N;
+  const int NS = gridDim.x;
+  const double inv_n = 1.0 / N;
+  const double pad = static_cast<double>(NS) * SPLIT_WG * EVE - N;
+  const double off = (OP == OP_LN) ? 0.0 : static_cast<double>(p.offset);
+
+  const rsrc_t rg = row_rsrc<SX>(p.dy, p.lddy, row, N);
+  const rsrc_t rx = row_rsrc<SX>(p.x, p.ldx, row, N);
+  const rsrc_t rw = make_rsrc(p.w, static_cast<uint32_t>(N) * sizeof(SW));
+  const int a0 = c * SPLIT_WG + t;
+  FX og, ox, od;
+  FW ow;
+  og.load(rg, a0, 0);
+  ox.load(rx, a0, 0);
+  ow.load(rw, a0, 0);
+  if constexpr (OP == OP_FADD) {
+    if (p.dres != nullptr) od.load(row_rsrc<SX>(p.dres, p.lddr, row, N), a0, 0);
+    else od.zero();
+  }
+  const double K = OP == OP_LN ? first_elem<DX>(rx) : 0.0;
+
+  // g = dy * (w + offset) in fp64 (the offset sum formed exactly), or the exact fp32
+  // product when XG
+  auto gval = [&](float dys, float w) -> double {
+    if constexpr (XG) return static_cast<double>(dys * w);
+    else if constexpr (OP == OP_LN) return static_cast<double>(dys) * static_cast<double>(w);
+    else {
+      const double dyd = static_cast<double>(dys);
+      return fma(dyd, static_cast<double>(w), dyd * off);
+    }
+  };
+
+  // statistics of the whole row: RMS sum x^2, sum g*x; LN sum d, sum d^2, sum g,
+  // sum g*d with d = x - K
+  constexpr int NA = OP == OP_LN ? 4 : 2;
+  double acc[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) acc[j] = 0.0;
+  for (int s0 = 0; s0 < NS; s0 += SPLIT_U) {
+    FX gs[SPLIT_U], xs[SPLIT_U];
+    FW ws[SPLIT_U];
+#pragma unroll
+    for (int u = 0; u < SPLIT_U; ++u) {
+      const int a = (s0 + u) * SPLIT_WG + t;
+      gs[u].load(rg, a, 0);
+      xs[u].load(rx, a, 0);
+      ws[u].load(rw, a, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < SPLIT_U; ++u) {
+      if (s0 + u >= NS) break;  // uniform
+#pragma unroll
+      for (int i = 0; i < EVE; ++i) {
+        const double g = gval(gs[u].get(i), ws[u].get(i));
+        if constexpr (OP == OP_LN) {
+          const double d = static_cast<double>(xs[u].get(i)) - K;
+          acc[0] += d;
+          acc[1] = fma(d, d, acc[1]);
+          acc[2] += g;
+          acc[3] = fma(g, d, acc[3]);
+        } else {
+          const double xd = static_cast<double>(xs[u].get(i));
+          acc[0] = fma(xd, xd, acc[0]);
+          acc[1] = fma(g, xd, acc[1]);
+        }
+      }
+    }
+  }
+  team_sum<NA>(acc, SPLIT_WG / 64, 0, red, parity);
+
+  float o[EVE], dwp[EVE];
+  if constexpr (OP == OP_LN) {
+    acc[0] = fma(pad, K, acc[0]);  // slots past N: d = -K, g = 0
+    acc[1] = fma(-pad * K, K, acc[1]);
+    const double delta = acc[0] * inv_n;  // mean - K
+    const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
+    const double rstd = rsqrt_d(var + static_cast<double>(p.eps));
+    const double mean = K + delta;
+    const double mg = acc[2] * inv_n;                // mean(g)
+    const double mgd = acc[3] * inv_n - delta * mg;  // mean(g * (x - mean))
+    // dx = rstd * (g - mean(g) - (x - mean) * rstd^2 * mean(g * (x - mean)))
+    const double c2 = mgd * rstd * rstd * rstd;
+    const double nmg = -mg * rstd;
+    const float rs = static_cast<float>(rstd);
+    const float nmr = static_cast<float>(-mean * rstd);
+#pragma unroll
+    for (int i = 0; i < EVE; ++i) {
+      const float xs = ox.get(i);
+      const double e = static_cast<double>(xs) - mean;
+      o[i] = static_cast<float>(fma(-e, c2, fma(gval(og.get(i), ow.get(i)), rstd, nmg)));
+      dwp[i] = og.get(i) * fmaf(xs, rs, nmr);
+    }
+  } else {
+    const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+    // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
+    const double cc = rstd * rstd * rstd * (acc[1] * inv_n);
+    const float rs = static_cast<float>(rstd);
+#pragma unroll
+    for (int i = 0; i < EVE; ++i) {
+      const float xs = ox.get(i);
+      double dxd = fma(-static_cast<double>(xs), cc, gval(og.get(i), ow.get(i)) * rstd);
+      if constexpr (OP == OP_FADD) dxd += static_cast<double>(od.get(i));
+      o[i] = static_cast<float>(dxd);
+      dwp[i] = og.get(i) * (xs * rs);
+    }
+  }
+  FX of;
+  of.pack(o);
+  of.store_raw(row_rsrc<SX>(p.dx, p.lddx, row, N), a0, 0);
+
+  // this span's products in partial row `row` (16-byte groups; N is a multiple of EVE,
+  // so an access lies wholly inside the row or wholly past it, where stores vanish)
+  auto put = [&](float* dst, const float (&v)[EVE]) {
+    const rsrc_t rd = make_rsrc(dst + row * p.ldws, static_cast<uint32_t>(N) * 4u);
+#pragma unroll
+    for (int q = 0; q < EVE / 4; ++q) {
+      const v4u w4 = {__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                      __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(w4, rd, (a0 * EVE + 4 * q) * 4, 0, 0);
+    }
+  };
+  if constexpr (CDW) put(p.pw, dwp);
+  if constexpr (CDB) {
+    float dbp[EVE];
+#pragma unroll
+    for (int i = 0; i < EVE; ++i) dbp[i] = og.get(i);
+    put(p.pb, dbp);
+  }
+}
+
+}  // namespace rn

@@ -95,6 +95,29 @@ def test_frozen_dx_bit_identical_and_dw_unchanged(op, io):
     del rn
 
 
+# Shapes whose frozen backward once took its own row layout (a frozen-only V for wide
+# rows and for the fused add): the layout now depends on the operation, N and the type
+# only, so dx is bit-identical by construction, fp32 outputs included.
+@pytest.mark.parametrize("case", [
+    ("fused_add_rmsnorm", 2048, 8192, "bf16", "bf16"),
+    ("fused_add_rmsnorm", 300, 8192, "fp32", "fp32"),
+    ("fused_add_rmsnorm", 200, 2000, "fp16", "fp16"),
+    ("rmsnorm", 128, 18432, "fp32", "fp32"),
+    ("rmsnorm", 128, 18432, "bf16", "fp32"),
+    ("layernorm", 64, 24576, "fp32", "fp32"),
+], ids=lambda c: f"{c[0]}_{c[1]}x{c[2]}_{c[3]}_{c[4]}")
+def test_frozen_dx_bit_identical_wide_and_fused(case):
+    op, m, n, io, wt = case
+    wl = workloads.small(op, m, n, io, wt, offset=1.0 if op != "layernorm" else 0.0,
+                         weight="gemma" if op != "layernorm" else "unit", seed=11)
+    _say("frozen layout", wl.name)
+    t = workloads.generate(wl)
+    full = gp.run_gpu(wl, t, dw=True, db=True)
+    frozen = gp.run_gpu(wl, t, dw=False, db=False)
+    bits = torch.int32 if io == "fp32" else torch.int16
+    assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
+
+
 @pytest.mark.parametrize("op", ["rmsnorm", "fused_add_rmsnorm"])
 def test_dw_independent_of_offset(op):
     # the offset is a constant of the weight: dw must not move with it

@@ -1,0 +1,126 @@
+"""GPU parity of the split-row kernels: a few long rows, each spread over several
+workgroups that all walk the whole row for its statistics (a decode row, a small
+batch).  Compared with the fp64 oracle element by element.  The same calls with the row
+kernels forced (a launch-shape override turns the split off) meet the same gates; dx
+with frozen parameters is bit-identical to dx with trainable ones; in-place calls, which
+must not take the split kernels, stay correct.
+
+Each case prints what it is before touching the GPU.
+"""
+import pytest
+import torch
+
+import workloads
+from tests import gpu_parity as gp
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import __graft_entry__
+    __graft_entry__.ensure_built()
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _wl(op, m, n, io, wt=None, gemma=False, **kw):
+    off = 1.0 if gemma else 0.0
+    return workloads.small(op, m, n, io, wt, offset=off, weight="gemma" if gemma else "unit",
+                           seed=500 + m + n % 97, **kw)
+
+
+# rows x 16-byte spans stay within 256 workgroups; N not a multiple of the span width
+# leaves a ragged last span
+CASES = [
+    _wl("rmsnorm", 1, 18432, "bf16", "fp32"),           # the decode row
+    _wl("rmsnorm", 1, 18432, "fp16"),
+    _wl("rmsnorm", 1, 18432, "fp32"),
+    _wl("rmsnorm", 1, 4096, "bf16", gemma=True),
+    _wl("rmsnorm", 2, 4104, "bf16", gemma=True),         # spans 2048 + 2048 + 8
+    _wl("rmsnorm", 128, 4096, "bf16", gemma=True),       # 256 workgroups
+    _wl("rmsnorm", 9, 24576, "fp32", "fp32"),            # 24 spans of 1024
+    _wl("layernorm", 1, 4096, "bf16"),
+    _wl("layernorm", 3, 8200, "bf16"),
+    _wl("layernorm", 16, 4104, "fp16", bias=False),
+    _wl("layernorm", 5, 24576, "fp32"),
+    _wl("layernorm", 2, 18432, "bf16", "fp32"),
+    _wl("fused_add_rmsnorm", 1, 18432, "bf16", gemma=True),
+    _wl("fused_add_rmsnorm", 4, 8192, "bf16", gemma=True),
+    _wl("fused_add_rmsnorm", 7, 12288, "fp16", "fp32", dres=False),
+    _wl("fused_add_rmsnorm", 3, 6144, "fp32"),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda c: c.name)
+def test_split_rows_against_oracle(wl):
+    _say(wl.name)
+    fails = gp.check(wl)
+    assert not fails, "\n".join(fails)
+
+
+@pytest.mark.parametrize("wl", CASES[::3], ids=lambda c: c.name)
+def test_row_kernels_forced_meet_the_same_gates(wl):
+    import normalization_row_wise_amd as rn
+    _say("row kernels forced", wl.name)
+    try:
+        for kind in (0, 1, 2):
+            rn.set_launch_override(kind, 0, 1, 0)   # any override turns the split off
+        fails = gp.check(wl)
+    finally:
+        for kind in (0, 1, 2):
+            rn.set_launch_override(kind, 0, 0, 0)
+    assert not fails, "\n".join(fails)
+
+
+@pytest.mark.parametrize("wl", CASES[::2], ids=lambda c: c.name)
+def test_split_frozen_dx_bit_identical(wl):
+    _say("split frozen vs trainable", wl.name)
+    t = workloads.generate(wl)
+    full = gp.run_gpu(wl, t, dw=True, db=True)
+    frozen = gp.run_gpu(wl, t, dw=False, db=False)
+    bits = gp._BITS_VIEW[wl.io]
+    assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
+    again = gp.run_gpu(wl, t, dw=True, db=True)
+    assert torch.equal(again["dw"], full["dw"])
+
+
+@pytest.mark.parametrize("op", ["rmsnorm", "layernorm", "fused_add_rmsnorm"])
+def test_inplace_calls_of_split_shapes(op):
+    """dx == dy and y == x on a shape that would be split: another workgroup of the row
+    would read what this one overwrites, so these calls take the row kernels."""
+    import normalization_row_wise_amd as rn
+    wl = _wl(op, 2, 8192, "bf16", gemma=op != "layernorm")
+    _say("in-place split shape", wl.name)
+    t = workloads.generate(wl)
+    o = gp.run_oracle(wl, t)
+    d = gp.to_device(t)
+    if op == "rmsnorm":
+        xin = d["x"].clone()
+        y, _ = rn.rmsnorm_fwd(xin, d["w"], t["eps"], t["offset"], y=xin)
+        dy = d["dy"].clone()
+        dx, dw = rn.rmsnorm_bwd(dy, d["x"], d["w"], t["eps"], t["offset"], dx=dy)
+    elif op == "layernorm":
+        xin = d["x"].clone()
+        y, _, _ = rn.layernorm_fwd(xin, d["w"], d["b"], t["eps"], y=xin)
+        dy = d["dy"].clone()
+        dx, dw, db = rn.layernorm_bwd(dy, d["x"], d["w"], t["eps"], dx=dy)
+    else:
+        res = d["residual"].clone()
+        y, ro, _ = rn.fused_add_rmsnorm_fwd(d["x"], res, d["w"], t["eps"], t["offset"],
+                                            residual_out=res)
+        dy = d["dy"].clone()
+        dx, dw = rn.fused_add_rmsnorm_bwd(dy, ro, d["w"], t["eps"], t["offset"], d["dres"],
+                                          dx=dy)
+        rep = gp.io_report(ro.cpu(), o["residual_out"], wl.io)
+        assert rep["max_ulp"] == 0, rep
+    torch.cuda.synchronize()
+    assert dx.data_ptr() == dy.data_ptr()
+    for k, g in (("y", y), ("dx", dx)):
+        rep = gp.io_report(g.cpu(), o[k], wl.io)
+        assert gp.io_ok(rep, wl.io), (k, rep)
+    assert gp.f32_report(dw.cpu(), o["dw"]) <= gp.REL_GRAD
