@@ -155,3 +155,33 @@ def test_noncontiguous_gradient():
     m(xd2).backward(big.t().contiguous())
     torch.cuda.synchronize()
     assert torch.equal(xd.grad.view(torch.int16), xd2.grad.view(torch.int16))
+
+
+@pytest.mark.parametrize("frozen", [False, True], ids=["trainable", "frozen"])
+def test_decode_row_module(frozen):
+    """One token of a wide model (the split-row kernels): y, dx and dw against the
+    oracle, with the weight trainable or frozen."""
+    from normalization_row_wise_amd.autograd import RMSNorm
+    _say("autograd decode row", "frozen" if frozen else "trainable")
+    g = torch.Generator().manual_seed(10)
+    N = 18432
+    x = torch.randn(1, 1, N, generator=g).to(torch.bfloat16)
+    dy = torch.randn(1, 1, N, generator=g).to(torch.bfloat16)
+    m = RMSNorm(N, eps=1e-6, device=gp.dev(), dtype=torch.float32)
+    with torch.no_grad():
+        m.weight.copy_(1 + 0.1 * torch.randn(N, generator=g))
+    m.weight.requires_grad_(not frozen)
+    xd = x.to(gp.dev()).requires_grad_(True)
+    y = m(xd)
+    y.backward(dy.to(gp.dev()))
+    torch.cuda.synchronize()
+    w64 = workloads.as_f64(m.weight.detach())
+    ry, _ = oracle.rmsnorm_fwd(_f64(x), w64, 1e-6, 0.0)
+    rdx, rdw = oracle.rmsnorm_bwd(_f64(dy), _f64(x), w64, 1e-6, 0.0)
+    _io_ok(y.detach(), ry)
+    _io_ok(xd.grad, rdx)
+    if frozen:
+        assert m.weight.grad is None
+    else:
+        assert m.weight.grad.dtype == torch.float32
+        assert gp.f32_report(m.weight.grad.cpu(), rdw) <= gp.REL_GRAD

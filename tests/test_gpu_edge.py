@@ -2,7 +2,8 @@
 (LayerNorm) or all zeros (RMSNorm), eps = 0, and magnitudes far from 1 (1e18 and 1e-18,
 where the mean square leaves the range of the fp32 reciprocal-square-root estimate and
 the kernels take the exact fp64 path).  Each row kind is mixed into one batch with
-ordinary rows, so every launch shape sees it.
+ordinary rows, so every launch shape sees it (the split-row kernels included: a few long
+rows).
 
 Each case prints what it is before touching the GPU.
 """
@@ -63,6 +64,11 @@ CASES = [
     ("layernorm", 300, 4096, "bf16", 0.0, "magnitude"),
     ("layernorm", 1000, 64, "fp32", 1e-5, "magnitude"),
     ("fused_add_rmsnorm", 300, 4096, "bf16", 1e-6, "magnitude"),
+    # few long rows: the split-row kernels
+    ("layernorm", 14, 8192, "bf16", 1e-5, "degenerate"),
+    ("fused_add_rmsnorm", 14, 8192, "bf16", 1e-6, "degenerate"),
+    ("rmsnorm", 14, 8192, "fp32", 0.0, "magnitude"),
+    ("layernorm", 12, 8192, "bf16", 0.0, "magnitude"),
 ]
 
 

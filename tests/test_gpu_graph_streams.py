@@ -100,6 +100,9 @@ GRAPH_CASES = [
     workloads.small("layernorm", 257, 4097, "bf16", seed=32),
     workloads.small("fused_add_rmsnorm", 130, 8192, "bf16", offset=1.0, weight="gemma", seed=33),
     workloads.small("rmsnorm", 64, 18432, "bf16", "fp32", seed=34),
+    # split rows (a decode row; a small LayerNorm batch): several workgroups per row
+    workloads.small("rmsnorm", 1, 18432, "bf16", "fp32", seed=35),
+    workloads.small("layernorm", 3, 8192, "bf16", seed=36),
 ]
 
 
