@@ -81,8 +81,12 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
     }
   };
 
-  // statistics of the whole row: RMS sum x^2; LN sum d, sum d^2 with d = x - K
-  double acc[2] = {0.0, 0.0};
+  // statistics of the whole row: RMS sum x^2; LN sum d, sum d^2 with d = x - K.  Span
+  // u of each batch adds into its own partial sums (independent chains of fp64 adds for
+  // a workgroup of one wave per SIMD), combined in a fixed order after the walk.
+  double part[SPLIT_U][2];
+#pragma unroll
+  for (int u = 0; u < SPLIT_U; ++u) part[u][0] = part[u][1] = 0.0;
   for (int s0 = 0; s0 < NS; s0 += SPLIT_U) {
     FX xs[SPLIT_U], rs[SPLIT_U];
 #pragma unroll
@@ -98,14 +102,20 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
       for (int i = 0; i < EVE; ++i) {
         if constexpr (OP == OP_LN) {
           const double d = static_cast<double>(xs[u].get(i)) - K;
-          acc[0] += d;
-          acc[1] = fma(d, d, acc[1]);
+          part[u][0] += d;
+          part[u][1] = fma(d, d, part[u][1]);
         } else {
           const double v = static_cast<double>(xs[u].get(i));
-          acc[0] = fma(v, v, acc[0]);
+          part[u][0] = fma(v, v, part[u][0]);
         }
       }
     }
+  }
+  double acc[2] = {part[0][0], part[0][1]};
+#pragma unroll
+  for (int u = 1; u < SPLIT_U; ++u) {
+    acc[0] += part[u][0];
+    acc[1] += part[u][1];
   }
   team_sum<2>(acc, SPLIT_WG / 64, 0, red, parity);
 
@@ -191,10 +201,14 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
 
   // statistics of the whole row: RMS sum x^2, sum g*x; LN sum d, sum d^2, sum g,
   // sum g*d with d = x - K
+  // (span u of each batch into its own partial sums, combined in a fixed order)
   constexpr int NA = OP == OP_LN ? 4 : 2;
-  double acc[NA];
+  double part[SPLIT_U][NA];
 #pragma unroll
-  for (int j = 0; j < NA; ++j) acc[j] = 0.0;
+  for (int u = 0; u < SPLIT_U; ++u) {
+#pragma unroll
+    for (int j = 0; j < NA; ++j) part[u][j] = 0.0;
+  }
   for (int s0 = 0; s0 < NS; s0 += SPLIT_U) {
     FX gs[SPLIT_U], xs[SPLIT_U];
     FW ws[SPLIT_U];
@@ -213,17 +227,24 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
         const double g = gval(gs[u].get(i), ws[u].get(i));
         if constexpr (OP == OP_LN) {
           const double d = static_cast<double>(xs[u].get(i)) - K;
-          acc[0] += d;
-          acc[1] = fma(d, d, acc[1]);
-          acc[2] += g;
-          acc[3] = fma(g, d, acc[3]);
+          part[u][0] += d;
+          part[u][1] = fma(d, d, part[u][1]);
+          part[u][2] += g;
+          part[u][3] = fma(g, d, part[u][3]);
         } else {
           const double xd = static_cast<double>(xs[u].get(i));
-          acc[0] = fma(xd, xd, acc[0]);
-          acc[1] = fma(g, xd, acc[1]);
+          part[u][0] = fma(xd, xd, part[u][0]);
+          part[u][1] = fma(g, xd, part[u][1]);
         }
       }
     }
+  }
+  double acc[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    acc[j] = part[0][j];
+#pragma unroll
+    for (int u = 1; u < SPLIT_U; ++u) acc[j] += part[u][j];
   }
   team_sum<NA>(acc, SPLIT_WG / 64, 0, red, parity);
 
