@@ -46,10 +46,10 @@
  *     in which each element is read before it is written by the same thread (never
  *     the split-row kernels, whose workgroups read the whole row).  Any other overlap
  *     is undefined.
- *   - Few long rows (aligned rows of at least two spans of 256 16-byte accesses, rows
- *     x spans <= 64 in the forward and <= 256 in the backward) are spread over several
- *     workgroups each; the results meet the same accuracy contract, and dx does not
- *     depend on which parameter gradients are requested.
+ *   - Few long rows (aligned rows of at least two spans of 256 16-byte accesses, at
+ *     most 128 rows) are spread over several workgroups each; the results meet the
+ *     same accuracy contract, and dx does not depend on which parameter gradients are
+ *     requested.
  */
 #ifndef ROWNORM_H
 #define ROWNORM_H

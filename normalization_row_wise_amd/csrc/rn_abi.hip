@@ -265,30 +265,38 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
   return s;
 }
 
-// Split rows (rn_split.h): each row spread over workgroups of SPLIT_WG threads, one per
-// 16-byte-access span of the row, when the rows are too few to keep the CUs busy one
-// team each (a decode row, a small batch).  Every workgroup walks its whole row for the
-// statistics, so a row takes at least two spans, and all rows' spans together stay
-// within one workgroup per CU.  The backward takes the same decision with and without
-// parameter gradients, so dx comes from the same kernel and the same sums either way;
-// its row kernels with gradients are slow at small M (few partial rows), hence the
-// wider bound.  The forward's redundant statistics cost more than they save beyond a
-// quarter of the CUs (measured: 28 rows of 18432 bf16, 4.8 us split against 4.2).
-// Needs 16-byte accesses and no output that is also an input; not taken while a
-// launch-shape override is set for the kind.  0: not split.
-#ifndef RN_SPLIT_MAX_WG_FWD
-#define RN_SPLIT_MAX_WG_FWD 64
+// Split rows (rn_split.h): each row spread over workgroups of SPLIT_WG threads when the
+// rows are too few to keep the CUs busy one team each (a decode row, a small batch).  A
+// row is cut into spans of SPLIT_WG 16-byte accesses; every workgroup walks its whole
+// row for the statistics and writes `spans` consecutive spans of the outputs.  A row
+// takes at least two workgroups, and all rows' workgroups together stay within one per
+// CU.  The backward takes the same decision with and without parameter gradients, so
+// dx comes from the same kernel and the same sums either way.  The forward, whose
+// output pass is light, gains nothing once a workgroup writes more than
+// kSplitFwdMaxSpans spans (128 fp32 rows of 18432: 2 workgroups of 9 spans each, 1 us
+// slower than one team per row; 128 bf16 rows of 18432, 5 spans each, 0.3-0.8 us
+// faster).  Needs 16-byte accesses and no output that is also an input; not taken
+// while a launch-shape override is set for the kind.
+#ifndef RN_SPLIT_MAX_WG
+#define RN_SPLIT_MAX_WG 256
 #endif
-#ifndef RN_SPLIT_MAX_WG_BWD
-#define RN_SPLIT_MAX_WG_BWD 256
-#endif
-inline int64_t split_spans(int kind, int64_t M, int64_t N, int eb, bool vec, bool aliased) {
+constexpr int64_t kSplitFwdMaxSpans = 5;
+struct Split {
+  int64_t wgs = 0;  // workgroups per row (0: rows not split)
+  int spans = 0;    // spans each workgroup writes
+};
+inline Split split_plan(int kind, int64_t M, int64_t N, int eb, bool vec, bool aliased) {
+  Split sp;
   const Override& o = g_override[kind];
-  if (!vec || aliased || o.v || o.rows || o.wg_rows) return 0;
-  const int64_t spans = cdiv(N, static_cast<int64_t>(SPLIT_WG) * (16 / eb));
-  const int64_t cap = kind == 0 ? RN_SPLIT_MAX_WG_FWD : RN_SPLIT_MAX_WG_BWD;
-  if (spans < 2 || M * spans > cap) return 0;
-  return spans;
+  if (!vec || aliased || o.v || o.rows || o.wg_rows) return sp;
+  const int64_t ns = cdiv(N, static_cast<int64_t>(SPLIT_WG) * (16 / eb));
+  const int64_t g = std::min<int64_t>(ns, RN_SPLIT_MAX_WG / M);
+  if (g < 2) return sp;
+  const int64_t k = cdiv(ns, g);
+  if (kind == 0 && k > kSplitFwdMaxSpans) return sp;
+  sp.spans = static_cast<int>(k);
+  sp.wgs = cdiv(ns, k);
+  return sp;
 }
 
 inline int launched() { return hipGetLastError() == hipSuccess ? RN_OK : RN_ERR_HIP; }
@@ -373,7 +381,7 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   int64_t max_ld = std::max(ldx, ldy);
   if (op == OP_FADD) max_ld = std::max({max_ld, ldr, ldro});
   const bool aliased = y == x || (op == OP_FADD && (y == res || ro == x || ro == res));
-  const int64_t spans = split_spans(0, M, N, eb, vec, aliased);
+  const Split sp = split_plan(0, M, N, eb, vec, aliased);
   const Shape s = plan(0, op, M, N, xt, 0, vec, M > 1 ? max_ld : N);
   FwdArgs a{};
   a.x = x; a.ldx = ldx; a.res = res; a.ldr = ldr; a.w = w; a.b = b;
@@ -381,11 +389,12 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   a.M = M; a.N = static_cast<int>(N); a.team = s.team;
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
+  a.spans_per_wg = sp.spans;
   Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
            dim3(static_cast<unsigned>(s.R * s.team)), 0, g_timing[0][0], g_timing[0][1]};
-  if (spans > 0) {
+  if (sp.wgs > 0) {
     l.split = true;
-    l.grid = dim3(static_cast<unsigned>(spans), static_cast<unsigned>(M));
+    l.grid = dim3(static_cast<unsigned>(sp.wgs), static_cast<unsigned>(M));
     l.block = dim3(SPLIT_WG);
   }
   bool ok = false;
@@ -453,10 +462,10 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   if (dres != nullptr) max_ld = std::max(max_ld, lddr);
   const int kind = ngrads > 0 ? 1 : 2;
   const bool aliased = dx == dy || dx == x || (dres != nullptr && dx == dres);
-  const int64_t spans = split_spans(kind, M, N, eb, vec, aliased);
+  const Split sp = split_plan(kind, M, N, eb, vec, aliased);
   const Shape s = plan(kind, op, M, N, xt, ngrads, vec, M > 1 ? max_ld : N);
   // partial rows: one per workgroup, or one per row when rows are split
-  const int P = spans > 0 ? static_cast<int>(M) : s.P;
+  const int P = sp.wgs > 0 ? static_cast<int>(M) : s.P;
   BwdArgs a{};
   a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
   a.dx = dx; a.lddx = lddx;
@@ -471,11 +480,12 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   a.M = M; a.N = static_cast<int>(N); a.team = s.team;
   a.rows_per_wg = static_cast<int>(s.rows_per_wg);
   a.eps = eps; a.offset = offset;
+  a.spans_per_wg = sp.spans;
   Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
            dim3(static_cast<unsigned>(s.R * s.team)), s.shmem, g_timing[1][0], g_timing[1][1]};
-  if (spans > 0) {
+  if (sp.wgs > 0) {
     l.split = true;
-    l.grid = dim3(static_cast<unsigned>(spans), static_cast<unsigned>(M));
+    l.grid = dim3(static_cast<unsigned>(sp.wgs), static_cast<unsigned>(M));
     l.block = dim3(SPLIT_WG);
     l.shmem = 0;
   }

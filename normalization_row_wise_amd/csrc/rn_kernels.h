@@ -42,6 +42,7 @@ struct FwdArgs {
   float* rstd; float* mean;         // may be null
   int64_t M; int N; int team; int rows_per_wg;
   float eps, offset;
+  int spans_per_wg;                 // split rows (rn_split.h): spans each workgroup writes
 };
 
 struct BwdArgs {
@@ -54,6 +55,7 @@ struct BwdArgs {
                                        // workgroup covers every row: dw and db themselves)
   int64_t M; int N; int team; int rows_per_wg;
   float eps, offset;
+  int spans_per_wg;                 // split rows (rn_split.h): spans each workgroup writes
 };
 
 // Register-budget policy (build-time tunable for launch-shape studies).

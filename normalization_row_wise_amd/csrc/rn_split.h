@@ -3,11 +3,13 @@
 //
 // With one team per row, a single row of 18432 elements is the serial work of one CU
 // (its fp64 passes alone take a few microseconds of that CU's vector ALUs) while the
-// other CUs idle.  Here workgroup (c, i) of SPLIT_WG threads owns span c of row i: the
-// columns of lane t's 16-byte access c * SPLIT_WG + t.  It first walks the whole row
-// and forms the row's sums itself, in the same order as every other workgroup of the
-// row, so all of them hold bitwise-identical statistics and none waits for another
-// (the redundant reads hit L2); then it writes its own span of the outputs.  The
+// other CUs idle.  Here a row is cut into spans of SPLIT_WG 16-byte accesses (span s:
+// lane t's access s * SPLIT_WG + t), and workgroup (c, i) of SPLIT_WG threads owns
+// the `spans_per_wg` consecutive spans from c * spans_per_wg of row i.  It first walks
+// the whole row and forms the row's sums itself, in the same order as every other
+// workgroup of the row, so all of them hold bitwise-identical statistics and none
+// waits for another (the redundant reads hit L2); then it writes its own spans of the
+// outputs (the first one preloaded before the walk, the others read again).  The
 // arithmetic is the one of the row kernels (rn_kernels.h): fp64 sums, LayerNorm y and
 // every dx formed in fp64 and rounded once, RMSNorm y in fp32 with the offset added to
 // the weight in fp32 ([gemma], Summary).
@@ -25,10 +27,10 @@
 namespace rn {
 
 #ifndef RN_SPLIT_U
-#define RN_SPLIT_U 4
+#define RN_SPLIT_U 2
 #endif
 constexpr int SPLIT_WG = 256;         // threads per workgroup
-constexpr int SPLIT_U = RN_SPLIT_U;   // spans a lane has in flight during the statistics walk
+constexpr int SPLIT_U = RN_SPLIT_U;   // spans per batch of the statistics walk (two batches in flight)
 
 // Buffer resource over row `row` of a row tensor (N elements of SX).
 template <typename SX>
@@ -36,7 +38,13 @@ __device__ __forceinline__ rsrc_t row_rsrc(const void* base, int64_t ld, int64_t
   return make_rsrc(static_cast<const SX*>(base) + row * ld, static_cast<uint32_t>(N) * sizeof(SX));
 }
 
-// Forward.  grid = (spans per row, M).
+// Number of spans of a row of N elements of DX.
+template <int DX> __device__ __forceinline__ int spans_of(int N) {
+  constexpr int S = SPLIT_WG * (16 / Ty<DX>::B);
+  return (N + S - 1) / S;
+}
+
+// Forward.  grid = (workgroups per row, M).
 template <int OP, int DX, int DW>
 __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
@@ -47,28 +55,33 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
   __shared__ double red[2][16][4];
   int parity = 0;
   const int t = threadIdx.x;
-  const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
   const int N = p.N;
-  const int NS = gridDim.x;
+  const int NS = spans_of<DX>(N);
+  const int s_first = blockIdx.x * p.spans_per_wg;
+  const int s_end = min(s_first + p.spans_per_wg, NS);
   const double inv_n = 1.0 / N;
   const double pad = static_cast<double>(NS) * SPLIT_WG * EVE - N;
 
   const rsrc_t rx = row_rsrc<SX>(p.x, p.ldx, row, N);
   rsrc_t rr = rx;
   if constexpr (OP == OP_FADD) rr = row_rsrc<SX>(p.res, p.ldr, row, N);
-  // this workgroup's span: inputs and parameters, loaded first
-  const int a0 = c * SPLIT_WG + t;
-  FX ox, orr;
-  FW ow, ob;
-  ox.load(rx, a0, 0);
-  if constexpr (OP == OP_FADD) orr.load(rr, a0, 0);
   const uint32_t par_bytes = static_cast<uint32_t>(N) * sizeof(SW);
-  ow.load(make_rsrc(p.w, par_bytes), a0, 0);
-  if constexpr (OP == OP_LN) {
-    if (p.b != nullptr) ob.load(make_rsrc(p.b, par_bytes), a0, 0);
-    else ob.zero();
-  }
+  const rsrc_t rw = make_rsrc(p.w, par_bytes);
+  const rsrc_t rb = make_rsrc(p.b, p.b != nullptr ? par_bytes : 0u);  // no bias: zeros
+  // inputs and parameters of one span of this workgroup
+  struct Own {
+    FX x, r;
+    FW w, b;
+  };
+  auto load_own = [&](Own& o, int a) {
+    o.x.load(rx, a, 0);
+    if constexpr (OP == OP_FADD) o.r.load(rr, a, 0);
+    o.w.load(rw, a, 0);
+    if constexpr (OP == OP_LN) o.b.load(rb, a, 0);
+  };
+  Own first;  // loaded before the walk
+  load_own(first, s_first * SPLIT_WG + t);
   const double K = OP == OP_LN ? first_elem<DX>(rx) : 0.0;
 
   // FusedAdd: the norm works on round(x + residual)
@@ -84,31 +97,48 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
   // statistics of the whole row: RMS sum x^2; LN sum d, sum d^2 with d = x - K.  Span
   // u of each batch adds into its own partial sums (independent chains of fp64 adds for
   // a workgroup of one wave per SIMD), combined in a fixed order after the walk.
+  // The walk takes SPLIT_U spans per batch and loads the next batch before adding the
+  // current one (loads past the row read zeros and are not added).
   double part[SPLIT_U][2];
 #pragma unroll
   for (int u = 0; u < SPLIT_U; ++u) part[u][0] = part[u][1] = 0.0;
-  for (int s0 = 0; s0 < NS; s0 += SPLIT_U) {
-    FX xs[SPLIT_U], rs[SPLIT_U];
+  struct Batch {
+    FX x[SPLIT_U], r[SPLIT_U];
+  };
+  auto load_batch = [&](Batch& b, int s0) {
 #pragma unroll
     for (int u = 0; u < SPLIT_U; ++u) {
-      xs[u].load(rx, (s0 + u) * SPLIT_WG + t, 0);
-      if constexpr (OP == OP_FADD) rs[u].load(rr, (s0 + u) * SPLIT_WG + t, 0);
+      b.x[u].load(rx, (s0 + u) * SPLIT_WG + t, 0);
+      if constexpr (OP == OP_FADD) b.r[u].load(rr, (s0 + u) * SPLIT_WG + t, 0);
     }
+  };
+  auto add_batch = [&](Batch& b, int s0) {
 #pragma unroll
     for (int u = 0; u < SPLIT_U; ++u) {
       if (s0 + u >= NS) break;  // uniform
-      summed(xs[u], rs[u]);
+      summed(b.x[u], b.r[u]);
 #pragma unroll
       for (int i = 0; i < EVE; ++i) {
         if constexpr (OP == OP_LN) {
-          const double d = static_cast<double>(xs[u].get(i)) - K;
+          const double d = static_cast<double>(b.x[u].get(i)) - K;
           part[u][0] += d;
           part[u][1] = fma(d, d, part[u][1]);
         } else {
-          const double v = static_cast<double>(xs[u].get(i));
+          const double v = static_cast<double>(b.x[u].get(i));
           part[u][0] = fma(v, v, part[u][0]);
         }
       }
+    }
+  };
+  {
+    Batch ba, bb;
+    load_batch(ba, 0);
+    for (int s0 = 0; s0 < NS; s0 += 2 * SPLIT_U) {
+      load_batch(bb, s0 + SPLIT_U);
+      add_batch(ba, s0);
+      if (s0 + SPLIT_U >= NS) break;
+      load_batch(ba, s0 + 2 * SPLIT_U);
+      add_batch(bb, s0 + SPLIT_U);
     }
   }
   double acc[2] = {part[0][0], part[0][1]};
@@ -119,40 +149,57 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
   }
   team_sum<2>(acc, SPLIT_WG / 64, 0, red, parity);
 
-  summed(ox, orr);
-  if constexpr (OP == OP_FADD) ox.store_raw(row_rsrc<SX>(p.ro, p.ldro, row, N), a0, 0);
-  float o[EVE];
+  double rstd, mean = 0.0;
   if constexpr (OP == OP_LN) {
     acc[0] = fma(pad, K, acc[0]);  // slots past N read as zero: d = -K each
     acc[1] = fma(-pad * K, K, acc[1]);
     const double delta = acc[0] * inv_n;
     const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
-    const double rstd = rsqrt_d(var + static_cast<double>(p.eps));
-    const double mean = K + delta;
-#pragma unroll
-    for (int i = 0; i < EVE; ++i) {
-      const double e = static_cast<double>(ox.get(i)) - mean;
-      o[i] = static_cast<float>(
-          fma(e * rstd, static_cast<double>(ow.get(i)), static_cast<double>(ob.get(i))));
-    }
-    if (c == 0 && t == 0) {
-      if (p.rstd != nullptr) p.rstd[row] = static_cast<float>(rstd);
+    rstd = rsqrt_d(var + static_cast<double>(p.eps));
+    mean = K + delta;
+  } else {
+    rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+  }
+  const float rs = static_cast<float>(rstd);
+  if (blockIdx.x == 0 && t == 0) {
+    if (p.rstd != nullptr) p.rstd[row] = rs;
+    if constexpr (OP == OP_LN) {
       if (p.mean != nullptr) p.mean[row] = static_cast<float>(mean);
     }
-  } else {
-    const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
-    const float rs = static_cast<float>(rstd);
-#pragma unroll
-    for (int i = 0; i < EVE; ++i) o[i] = (ox.get(i) * rs) * (ow.get(i) + p.offset);
-    if (c == 0 && t == 0 && p.rstd != nullptr) p.rstd[row] = rs;
   }
-  FX yf;
-  yf.pack(o);
-  yf.store_raw(row_rsrc<SX>(p.y, p.ldy, row, N), a0, 0);
+  const rsrc_t ry = row_rsrc<SX>(p.y, p.ldy, row, N);
+  auto emit = [&](Own& in, int a) {
+    summed(in.x, in.r);
+    if constexpr (OP == OP_FADD) in.x.store_raw(row_rsrc<SX>(p.ro, p.ldro, row, N), a, 0);
+    float o[EVE];
+#pragma unroll
+    for (int i = 0; i < EVE; ++i) {
+      if constexpr (OP == OP_LN) {
+        const double e = static_cast<double>(in.x.get(i)) - mean;
+        o[i] = static_cast<float>(fma(e * rstd, static_cast<double>(in.w.get(i)),
+                                      static_cast<double>(in.b.get(i))));
+      } else {
+        o[i] = (in.x.get(i) * rs) * (in.w.get(i) + p.offset);
+      }
+    }
+    FX yf;
+    yf.pack(o);
+    yf.store_raw(ry, a, 0);
+  };
+  // the later spans are read again, each one's loads issued before the previous span
+  // is written (a load past this workgroup's spans, or past the row, is harmless)
+  Own cur = first;
+#pragma unroll 1
+  for (int sp = s_first; sp < s_end; ++sp) {
+    Own nxt;
+    load_own(nxt, (sp + 1) * SPLIT_WG + t);
+    emit(cur, sp * SPLIT_WG + t);
+    cur = nxt;
+  }
 }
 
-// Backward (stage 1).  grid = (spans per row, M).  pw / pb: row i of the partial rows
-// (stride ldws), or dw / db themselves when M = 1.
+// Backward (stage 1).  grid = (workgroups per row, M).  pw / pb: row i of the partial
+// rows (stride ldws), or dw / db themselves when M = 1.
 template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG>
 __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
@@ -165,10 +212,11 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   __shared__ double red[2][16][4];
   int parity = 0;
   const int t = threadIdx.x;
-  const int c = blockIdx.x;
   const int64_t row = blockIdx.y;
   const int N = p.N;
-  const int NS = gridDim.x;
+  const int NS = spans_of<DX>(N);
+  const int s_first = blockIdx.x * p.spans_per_wg;
+  const int s_end = min(s_first + p.spans_per_wg, NS);
   const double inv_n = 1.0 / N;
   const double pad = static_cast<double>(NS) * SPLIT_WG * EVE - N;
   const double off = (OP == OP_LN) ? 0.0 : static_cast<double>(p.offset);
@@ -176,16 +224,22 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   const rsrc_t rg = row_rsrc<SX>(p.dy, p.lddy, row, N);
   const rsrc_t rx = row_rsrc<SX>(p.x, p.ldx, row, N);
   const rsrc_t rw = make_rsrc(p.w, static_cast<uint32_t>(N) * sizeof(SW));
-  const int a0 = c * SPLIT_WG + t;
-  FX og, ox, od;
-  FW ow;
-  og.load(rg, a0, 0);
-  ox.load(rx, a0, 0);
-  ow.load(rw, a0, 0);
-  if constexpr (OP == OP_FADD) {
-    if (p.dres != nullptr) od.load(row_rsrc<SX>(p.dres, p.lddr, row, N), a0, 0);
-    else od.zero();
-  }
+  // no residual-output gradient: a zero-byte resource reads zeros
+  const rsrc_t rd = OP == OP_FADD && p.dres != nullptr ? row_rsrc<SX>(p.dres, p.lddr, row, N)
+                                                       : make_rsrc(p.dy, 0u);
+  // inputs and weight of one span of this workgroup
+  struct Own {
+    FX g, x, d;
+    FW w;
+  };
+  auto load_own = [&](Own& o, int a) {
+    o.g.load(rg, a, 0);
+    o.x.load(rx, a, 0);
+    o.w.load(rw, a, 0);
+    if constexpr (OP == OP_FADD) o.d.load(rd, a, 0);
+  };
+  Own first;  // loaded before the walk
+  load_own(first, s_first * SPLIT_WG + t);
   const double K = OP == OP_LN ? first_elem<DX>(rx) : 0.0;
 
   // g = dy * (w + offset) in fp64 (the offset sum formed exactly), or the exact fp32
@@ -200,8 +254,8 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   };
 
   // statistics of the whole row: RMS sum x^2, sum g*x; LN sum d, sum d^2, sum g,
-  // sum g*d with d = x - K
-  // (span u of each batch into its own partial sums, combined in a fixed order)
+  // sum g*d with d = x - K (walked as in the forward: span u of each batch into its own
+  // partial sums, combined in a fixed order; the next batch loaded before adding one)
   constexpr int NA = OP == OP_LN ? 4 : 2;
   double part[SPLIT_U][NA];
 #pragma unroll
@@ -209,34 +263,49 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
 #pragma unroll
     for (int j = 0; j < NA; ++j) part[u][j] = 0.0;
   }
-  for (int s0 = 0; s0 < NS; s0 += SPLIT_U) {
-    FX gs[SPLIT_U], xs[SPLIT_U];
-    FW ws[SPLIT_U];
+  struct Batch {
+    FX g[SPLIT_U], x[SPLIT_U];
+    FW w[SPLIT_U];
+  };
+  auto load_batch = [&](Batch& b, int s0) {
 #pragma unroll
     for (int u = 0; u < SPLIT_U; ++u) {
       const int a = (s0 + u) * SPLIT_WG + t;
-      gs[u].load(rg, a, 0);
-      xs[u].load(rx, a, 0);
-      ws[u].load(rw, a, 0);
+      b.g[u].load(rg, a, 0);
+      b.x[u].load(rx, a, 0);
+      b.w[u].load(rw, a, 0);
     }
+  };
+  auto add_batch = [&](const Batch& b, int s0) {
 #pragma unroll
     for (int u = 0; u < SPLIT_U; ++u) {
       if (s0 + u >= NS) break;  // uniform
 #pragma unroll
       for (int i = 0; i < EVE; ++i) {
-        const double g = gval(gs[u].get(i), ws[u].get(i));
+        const double g = gval(b.g[u].get(i), b.w[u].get(i));
         if constexpr (OP == OP_LN) {
-          const double d = static_cast<double>(xs[u].get(i)) - K;
+          const double d = static_cast<double>(b.x[u].get(i)) - K;
           part[u][0] += d;
           part[u][1] = fma(d, d, part[u][1]);
           part[u][2] += g;
           part[u][3] = fma(g, d, part[u][3]);
         } else {
-          const double xd = static_cast<double>(xs[u].get(i));
+          const double xd = static_cast<double>(b.x[u].get(i));
           part[u][0] = fma(xd, xd, part[u][0]);
           part[u][1] = fma(g, xd, part[u][1]);
         }
       }
+    }
+  };
+  {
+    Batch ba, bb;
+    load_batch(ba, 0);
+    for (int s0 = 0; s0 < NS; s0 += 2 * SPLIT_U) {
+      load_batch(bb, s0 + SPLIT_U);
+      add_batch(ba, s0);
+      if (s0 + SPLIT_U >= NS) break;
+      load_batch(ba, s0 + 2 * SPLIT_U);
+      add_batch(bb, s0 + SPLIT_U);
     }
   }
   double acc[NA];
@@ -248,63 +317,74 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   }
   team_sum<NA>(acc, SPLIT_WG / 64, 0, red, parity);
 
-  float o[EVE], dwp[EVE];
+  // row constants: dx = rstd * g + c0 - x * cx (LN: c0 = -mean(g) * rstd and x taken
+  // as x - mean; RMS: c0 = 0); xhat = x * rs + nmr (nmr = 0 for RMS)
+  double rstd, cx, c0 = 0.0, mean = 0.0;
   if constexpr (OP == OP_LN) {
     acc[0] = fma(pad, K, acc[0]);  // slots past N: d = -K, g = 0
     acc[1] = fma(-pad * K, K, acc[1]);
     const double delta = acc[0] * inv_n;  // mean - K
     const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
-    const double rstd = rsqrt_d(var + static_cast<double>(p.eps));
-    const double mean = K + delta;
+    rstd = rsqrt_d(var + static_cast<double>(p.eps));
+    mean = K + delta;
     const double mg = acc[2] * inv_n;                // mean(g)
     const double mgd = acc[3] * inv_n - delta * mg;  // mean(g * (x - mean))
     // dx = rstd * (g - mean(g) - (x - mean) * rstd^2 * mean(g * (x - mean)))
-    const double c2 = mgd * rstd * rstd * rstd;
-    const double nmg = -mg * rstd;
-    const float rs = static_cast<float>(rstd);
-    const float nmr = static_cast<float>(-mean * rstd);
-#pragma unroll
-    for (int i = 0; i < EVE; ++i) {
-      const float xs = ox.get(i);
-      const double e = static_cast<double>(xs) - mean;
-      o[i] = static_cast<float>(fma(-e, c2, fma(gval(og.get(i), ow.get(i)), rstd, nmg)));
-      dwp[i] = og.get(i) * fmaf(xs, rs, nmr);
-    }
+    cx = mgd * rstd * rstd * rstd;
+    c0 = -mg * rstd;
   } else {
-    const double rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+    rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
     // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
-    const double cc = rstd * rstd * rstd * (acc[1] * inv_n);
-    const float rs = static_cast<float>(rstd);
-#pragma unroll
-    for (int i = 0; i < EVE; ++i) {
-      const float xs = ox.get(i);
-      double dxd = fma(-static_cast<double>(xs), cc, gval(og.get(i), ow.get(i)) * rstd);
-      if constexpr (OP == OP_FADD) dxd += static_cast<double>(od.get(i));
-      o[i] = static_cast<float>(dxd);
-      dwp[i] = og.get(i) * (xs * rs);
-    }
+    cx = rstd * rstd * rstd * (acc[1] * inv_n);
   }
-  FX of;
-  of.pack(o);
-  of.store_raw(row_rsrc<SX>(p.dx, p.lddx, row, N), a0, 0);
-
-  // this span's products in partial row `row` (16-byte groups; N is a multiple of EVE,
-  // so an access lies wholly inside the row or wholly past it, where stores vanish)
-  auto put = [&](float* dst, const float (&v)[EVE]) {
-    const rsrc_t rd = make_rsrc(dst + row * p.ldws, static_cast<uint32_t>(N) * 4u);
+  const float rs = static_cast<float>(rstd);
+  const float nmr = static_cast<float>(-mean * rstd);
+  const rsrc_t rdx = row_rsrc<SX>(p.dx, p.lddx, row, N);
+  // a span's products go to partial row `row` as 16-byte groups (N is a multiple of
+  // EVE, so an access lies wholly inside the row or wholly past it, where stores vanish)
+  auto put = [&](float* dst, const float (&v)[EVE], int a) {
+    const rsrc_t rp = make_rsrc(dst + row * p.ldws, static_cast<uint32_t>(N) * 4u);
 #pragma unroll
     for (int q = 0; q < EVE / 4; ++q) {
       const v4u w4 = {__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
                       __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
-      __builtin_amdgcn_raw_buffer_store_b128(w4, rd, (a0 * EVE + 4 * q) * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(w4, rp, (a * EVE + 4 * q) * 4, 0, 0);
     }
   };
-  if constexpr (CDW) put(p.pw, dwp);
-  if constexpr (CDB) {
-    float dbp[EVE];
+  auto emit = [&](const Own& in, int a) {
+    float o[EVE], dwp[EVE], dbp[EVE];
 #pragma unroll
-    for (int i = 0; i < EVE; ++i) dbp[i] = og.get(i);
-    put(p.pb, dbp);
+    for (int i = 0; i < EVE; ++i) {
+      const float xs = in.x.get(i);
+      const float dys = in.g.get(i);
+      const double g = gval(dys, in.w.get(i));
+      if constexpr (OP == OP_LN) {
+        const double e = static_cast<double>(xs) - mean;
+        o[i] = static_cast<float>(fma(-e, cx, fma(g, rstd, c0)));
+        dwp[i] = dys * fmaf(xs, rs, nmr);
+      } else {
+        double dxd = fma(-static_cast<double>(xs), cx, g * rstd);
+        if constexpr (OP == OP_FADD) dxd += static_cast<double>(in.d.get(i));
+        o[i] = static_cast<float>(dxd);
+        dwp[i] = dys * (xs * rs);
+      }
+      dbp[i] = dys;
+    }
+    FX of;
+    of.pack(o);
+    of.store_raw(rdx, a, 0);
+    if constexpr (CDW) put(p.pw, dwp, a);
+    if constexpr (CDB) put(p.pb, dbp, a);
+  };
+  // the later spans are read again, each one's loads issued before the previous span
+  // is written (a load past this workgroup's spans, or past the row, is harmless)
+  Own cur = first;
+#pragma unroll 1
+  for (int sp = s_first; sp < s_end; ++sp) {
+    Own nxt;
+    load_own(nxt, (sp + 1) * SPLIT_WG + t);
+    emit(cur, sp * SPLIT_WG + t);
+    cur = nxt;
   }
 }
 

@@ -34,8 +34,9 @@ def _wl(op, m, n, io, wt=None, gemma=False, **kw):
                            seed=500 + m + n % 97, **kw)
 
 
-# rows x 16-byte spans stay within 256 workgroups; N not a multiple of the span width
-# leaves a ragged last span
+# Spans are 256 16-byte accesses (2048 elements of a 16-bit type, 1024 of fp32); N not a
+# multiple of that leaves a ragged last span.  Rows of many spans at larger row counts
+# give each workgroup a run of several spans (the later ones read again after the walk).
 CASES = [
     _wl("rmsnorm", 1, 18432, "bf16", "fp32"),           # the decode row
     _wl("rmsnorm", 1, 18432, "fp16"),
@@ -53,6 +54,12 @@ CASES = [
     _wl("fused_add_rmsnorm", 4, 8192, "bf16", gemma=True),
     _wl("fused_add_rmsnorm", 7, 12288, "fp16", "fp32", dres=False),
     _wl("fused_add_rmsnorm", 3, 6144, "fp32"),
+    _wl("rmsnorm", 128, 18432, "bf16", "fp32"),          # 2 workgroups of 5 / 4 spans
+    _wl("rmsnorm", 128, 18432, "fp32"),                  # backward: 2 of 9 spans
+    _wl("rmsnorm", 16, 18432, "fp16", gemma=True),
+    _wl("layernorm", 100, 8200, "bf16"),                 # 2 of 3 / 2 spans, ragged
+    _wl("layernorm", 20, 24576, "fp32", bias=False),     # 12 of 2 spans
+    _wl("fused_add_rmsnorm", 60, 12288, "bf16", gemma=True),  # 3 of 2 spans
 ]
 
 
