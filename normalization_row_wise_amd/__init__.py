@@ -69,7 +69,16 @@ def _check(status: int) -> None:
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor on the current GPU (the kernels would fault on a host
+    address or on another device's memory, so anything else is refused here)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("every tensor argument must be a GPU tensor (got one on the CPU)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _rows(t, name):

@@ -121,3 +121,17 @@ def test_launch_override_validation(rn):
     assert L.rn_set_launch_override(0, 12, 0, 0) == E_SHAPE       # not a compiled V
     assert L.rn_set_launch_override(0, 16, 2, 0) == RN_OK
     assert L.rn_set_launch_override(0, 0, 0, 0) == RN_OK          # back to automatic
+
+
+def test_binding_refuses_host_tensors(rn):
+    """A host address handed to a kernel would fault the GPU: the binding refuses CPU
+    tensors before anything reaches the library."""
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.rmsnorm_fwd(x, w)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.layernorm_bwd(x, x, w)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.fused_add_rmsnorm_fwd(x, x, w)
