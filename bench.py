@@ -292,9 +292,9 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard across GPUs with no communication except one dW/dB all-reduce; "
-              "see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (rows "
+              "would shard across GPUs with no communication except one all-reduce of "
+              "dW/dB).", file=sys.stderr)
         sys.exit(2)
 
     import torch
