@@ -226,6 +226,42 @@ def event_times(sets, n, rn, torch):
             "bwd_stage1_us_mean": mean(b1), "fwd_us_mean": mean(f)}
 
 
+def stream_ceiling(sets, n, torch) -> dict:
+    """Context for the stage-1 roofline: torch's own elementwise kernel moving the same
+    row tensors as the backward's first kernel (2 reads + 1 write; the fused add's 3 + 1),
+    on the same rotating buffer sets, timed like the library's kernels (events around
+    each launch, queued behind a spin kernel).  No reduction, no fp64: what streaming
+    alone reaches on this GPU for this size."""
+    fused = sets.wl.op == "fused_add_rmsnorm"
+    st = torch.cuda.current_stream()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[mk(), mk()] for _ in range(n)]
+    for e in (x for row in ev for x in row):
+        e.record(st)
+
+    def op(k):
+        d = sets.sets[(k + sets.S // 2) % sets.S]
+        if fused:
+            torch.addcmul(d["dres"], d["dy"], d["ro"], out=d["dx"])
+        else:
+            torch.mul(d["dy"], d["x"], out=d["dx"])
+
+    for k in range(3):
+        op(k)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2.4e9 * (0.002 + 20e-6 * n)))
+    for k in range(n):
+        ev[k][0].record(st)
+        op(k)
+        ev[k][1].record(st)
+    torch.cuda.synchronize()
+    t = sorted(ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(n))[n // 2]
+    x = sets.sets[0]["x"]
+    nbytes = x.numel() * x.element_size() * (4 if fused else 3)
+    return {"op": "torch.addcmul, 3 reads + 1 write" if fused else "torch.mul, 2 reads + 1 write",
+            "us_median": round(t, 3), "gbs": round(nbytes / (t * 1e-6) / 1e9, 1)}
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The oracle (numpy fp64, as it stands) on a bounded sample of the workload's rows,
     forward + backward, repeated until `budget_s` of CPU time has passed."""
@@ -326,6 +362,8 @@ def main():
                  "frozen_bwd_kernel_us": round(fev["bwd_stage1_us_median"], 3)}
         del fz
 
+    ceiling = stream_ceiling(sets, args.event_steps, torch) if "dres" in sets.sets[0] or \
+        sets.wl.op != "fused_add_rmsnorm" else None
     stage1_us = ev["bwd_stage1_us_mean"]
     achieved = ab["bwd_stage1"] / (stage1_us * 1e-6) / 1e9
     kernel_key = "bwd_stage1_trainable" if trainable else "bwd_frozen"
@@ -360,7 +398,8 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "alg_bytes_per_launch": ab["bwd_stage1"],
-                     "avg_launch_us": round(stage1_us, 3)},
+                     "avg_launch_us": round(stage1_us, 3),
+                     "stream_ceiling": ceiling},
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
