@@ -60,6 +60,9 @@ CASES = [
     _wl("layernorm", 100, 8200, "bf16"),                 # 2 of 3 / 2 spans, ragged
     _wl("layernorm", 20, 24576, "fp32", bias=False),     # 12 of 2 spans
     _wl("fused_add_rmsnorm", 60, 12288, "bf16", gemma=True),  # 3 of 2 spans
+    _wl("layernorm", 7, 1028, "fp32"),                   # spans of 1024 + 4
+    _wl("rmsnorm", 3, 2056, "fp16", "fp32", gemma=True),  # spans of 2048 + 8
+    _wl("fused_add_rmsnorm", 128, 4104, "fp16", gemma=True),  # 2 of 2 / 1 spans
 ]
 
 
