@@ -185,3 +185,47 @@ def test_decode_row_module(frozen):
     else:
         assert m.weight.grad.dtype == torch.float32
         assert gp.f32_report(m.weight.grad.cpu(), rdw) <= gp.REL_GRAD
+
+
+@pytest.mark.parametrize("in_place", [False, True], ids=["out_of_place", "in_place"])
+def test_page_call_signature(in_place):
+    """The call of the Gemma page's reproduction, (x, w, eps, offset, casting_mode,
+    in_place, row_mode), on its 128 x 4096 bf16 problem, against the oracle."""
+    from normalization_row_wise_amd.autograd import RMSNormFunction
+    _say("autograd page call", "in place" if in_place else "out of place")
+    g = torch.Generator().manual_seed(42)
+    x = torch.randn(128, 4096, generator=g).to(torch.bfloat16)
+    w = (torch.randn(4096, generator=g) * 0.01).to(torch.bfloat16)
+    dy = torch.randn(128, 4096, generator=g).to(torch.bfloat16)
+    xd = x.to(gp.dev()).requires_grad_(True)
+    wd = w.to(gp.dev()).requires_grad_(True)
+    y = RMSNormFunction.apply(xd, wd, 1e-6, 1.0, "gemma", in_place, None)
+    gx, gw = torch.autograd.grad(y, (xd, wd), dy.to(gp.dev()))
+    torch.cuda.synchronize()
+    w64 = workloads.as_f64(w)
+    ry, _ = oracle.rmsnorm_fwd(_f64(x), w64, 1e-6, 1.0)
+    rdx, rdw = oracle.rmsnorm_bwd(_f64(dy), _f64(x), w64, 1e-6, 1.0)
+    _io_ok(y.detach(), ry)
+    _io_ok(gx, rdx)
+    _grad_ok(gw, rdw)
+    with pytest.raises(ValueError):
+        RMSNormFunction.apply(xd, wd, 1e-6, 1.0, "llama", False, None)
+
+
+def test_gradient_broadcast_along_rows():
+    """y.sum(0) sends the same gradient row to every row (a zero row stride): the binding
+    copies it instead of handing overlapping rows to the kernels."""
+    from normalization_row_wise_amd.autograd import LayerNorm
+    _say("autograd broadcast gradient")
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn(64, 1024, generator=g).to(torch.bfloat16).to(gp.dev())
+    up = torch.randn(1024, generator=g).to(torch.bfloat16).to(gp.dev())
+    m = LayerNorm(1024, device=gp.dev())
+    xd = x.clone().requires_grad_(True)
+    (m(xd).sum(0) * up).sum().backward()
+    xd2 = x.clone().requires_grad_(True)
+    m2 = LayerNorm(1024, device=gp.dev())
+    m2(xd2).backward(up.expand(64, 1024).contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(xd.grad.view(torch.int16), xd2.grad.view(torch.int16))
+    assert torch.equal(m.weight.grad, m2.weight.grad)
