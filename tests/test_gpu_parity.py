@@ -40,6 +40,22 @@ def test_named_workload(wl):
     assert not fails, "\n".join(fails)
 
 
+# Maximum sizes: a million rows of 8 (the narrow path's grid-stride limits) and rows of
+# the widest N at thousands of rows; outputs checked on sampled rows, dW / dB in full.
+LARGE = [
+    workloads.small("rmsnorm", 2**20 + 3, 8, "bf16", offset=1.0, weight="gemma", seed=71),
+    workloads.small("layernorm", 3001, 24576, "bf16", seed=72),
+    workloads.small("fused_add_rmsnorm", 1500, 24576, "fp32", seed=73),
+]
+
+
+@pytest.mark.parametrize("wl", LARGE, ids=lambda c: c.name)
+def test_largest_shapes(wl):
+    _say(wl.name)
+    fails = gp.check(wl, sample_rows=1024)
+    assert not fails, "\n".join(fails)
+
+
 # ---- ragged shapes, several tiles, every type pair -----------------------------------
 
 RAGGED_N = [1, 7, 64, 100, 511, 512, 513, 1000, 1024, 2050, 4095, 4096, 4097, 8191, 8193,
