@@ -270,17 +270,13 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
 // row is cut into spans of SPLIT_WG 16-byte accesses; every workgroup walks its whole
 // row for the statistics and writes `spans` consecutive spans of the outputs.  A row
 // takes at least two workgroups, and all rows' workgroups together stay within one per
-// CU.  The backward takes the same decision with and without parameter gradients, so
-// dx comes from the same kernel and the same sums either way.  The forward, whose
-// output pass is light, gains nothing once a workgroup writes more than
-// kSplitFwdMaxSpans spans (128 fp32 rows of 18432: 2 workgroups of 9 spans each, 1 us
-// slower than one team per row; 128 bf16 rows of 18432, 5 spans each, 0.3-0.8 us
-// faster).  Needs 16-byte accesses and no output that is also an input; not taken
-// while a launch-shape override is set for the kind.
+// CU (so at most 128 rows).  The forward and both backward forms take the same
+// decision; in the backward that makes dx come from the same kernel and the same sums
+// with and without parameter gradients.  Needs 16-byte accesses and no output that is
+// also an input; not taken while a launch-shape override is set for the kind.
 #ifndef RN_SPLIT_MAX_WG
 #define RN_SPLIT_MAX_WG 256
 #endif
-constexpr int64_t kSplitFwdMaxSpans = 5;
 struct Split {
   int64_t wgs = 0;  // workgroups per row (0: rows not split)
   int spans = 0;    // spans each workgroup writes
@@ -293,7 +289,6 @@ inline Split split_plan(int kind, int64_t M, int64_t N, int eb, bool vec, bool a
   const int64_t g = std::min<int64_t>(ns, RN_SPLIT_MAX_WG / M);
   if (g < 2) return sp;
   const int64_t k = cdiv(ns, g);
-  if (kind == 0 && k > kSplitFwdMaxSpans) return sp;
   sp.spans = static_cast<int>(k);
   sp.wgs = cdiv(ns, k);
   return sp;

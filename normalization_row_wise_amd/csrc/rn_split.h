@@ -9,7 +9,8 @@
 // the whole row and forms the row's sums itself, in the same order as every other
 // workgroup of the row, so all of them hold bitwise-identical statistics and none
 // waits for another (the redundant reads hit L2); then it writes its own spans of the
-// outputs (the first one preloaded before the walk, the others read again).  The
+// outputs (the first one loaded before the walk, the next ones read again while the
+// row's sums are reduced).  The
 // arithmetic is the one of the row kernels (rn_kernels.h): fp64 sums, LayerNorm y and
 // every dx formed in fp64 and rounded once, RMSNorm y in fp32 with the offset added to
 // the weight in fp32 ([gemma], Summary).
@@ -31,6 +32,14 @@ namespace rn {
 #endif
 constexpr int SPLIT_WG = 256;         // threads per workgroup
 constexpr int SPLIT_U = RN_SPLIT_U;   // spans per batch of the statistics walk (two batches in flight)
+#ifndef RN_SPLIT_AHEAD
+#define RN_SPLIT_AHEAD 4
+#endif
+// A workgroup's spans after the first: this many are read together right after the walk
+// (their latency then overlaps the row reduction); any further ones one ahead of use.
+constexpr int SPLIT_AHEAD = RN_SPLIT_AHEAD;
+
+template <bool B> struct SplitMore { static constexpr bool value = B; };
 
 // Buffer resource over row `row` of a row tensor (N elements of SX).
 template <typename SX>
@@ -147,55 +156,79 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
     acc[0] += part[u][0];
     acc[1] += part[u][1];
   }
-  team_sum<2>(acc, SPLIT_WG / 64, 0, red, parity);
-
-  double rstd, mean = 0.0;
-  if constexpr (OP == OP_LN) {
-    acc[0] = fma(pad, K, acc[0]);  // slots past N read as zero: d = -K each
-    acc[1] = fma(-pad * K, K, acc[1]);
-    const double delta = acc[0] * inv_n;
-    const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
-    rstd = rsqrt_d(var + static_cast<double>(p.eps));
-    mean = K + delta;
-  } else {
-    rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
-  }
-  const float rs = static_cast<float>(rstd);
-  if (blockIdx.x == 0 && t == 0) {
-    if (p.rstd != nullptr) p.rstd[row] = rs;
-    if constexpr (OP == OP_LN) {
-      if (p.mean != nullptr) p.mean[row] = static_cast<float>(mean);
-    }
-  }
-  const rsrc_t ry = row_rsrc<SX>(p.y, p.ldy, row, N);
-  auto emit = [&](Own& in, int a) {
-    summed(in.x, in.r);
-    if constexpr (OP == OP_FADD) in.x.store_raw(row_rsrc<SX>(p.ro, p.ldro, row, N), a, 0);
-    float o[EVE];
+  // Reduction and output.  A workgroup of several spans reads the next ones (loads past
+  // its spans or the row are harmless and unused) while the row's sums are reduced; a
+  // one-span workgroup (a decode row) issues no such loads.  The two are separate code
+  // paths, so neither waits for loads it does not use.
+  auto finish = [&](auto more) {
+    constexpr bool MORE = decltype(more)::value;
+    Own ahead[MORE ? SPLIT_AHEAD : 1];
+    if constexpr (MORE) {
 #pragma unroll
-    for (int i = 0; i < EVE; ++i) {
+      for (int k = 0; k < SPLIT_AHEAD; ++k) load_own(ahead[k], (s_first + 1 + k) * SPLIT_WG + t);
+    }
+    team_sum<2>(acc, SPLIT_WG / 64, 0, red, parity);
+
+    double rstd, mean = 0.0;
+    if constexpr (OP == OP_LN) {
+      acc[0] = fma(pad, K, acc[0]);  // slots past N read as zero: d = -K each
+      acc[1] = fma(-pad * K, K, acc[1]);
+      const double delta = acc[0] * inv_n;
+      const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
+      rstd = rsqrt_d(var + static_cast<double>(p.eps));
+      mean = K + delta;
+    } else {
+      rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+    }
+    const float rs = static_cast<float>(rstd);
+    if (blockIdx.x == 0 && t == 0) {
+      if (p.rstd != nullptr) p.rstd[row] = rs;
       if constexpr (OP == OP_LN) {
-        const double e = static_cast<double>(in.x.get(i)) - mean;
-        o[i] = static_cast<float>(fma(e * rstd, static_cast<double>(in.w.get(i)),
-                                      static_cast<double>(in.b.get(i))));
-      } else {
-        o[i] = (in.x.get(i) * rs) * (in.w.get(i) + p.offset);
+        if (p.mean != nullptr) p.mean[row] = static_cast<float>(mean);
       }
     }
-    FX yf;
-    yf.pack(o);
-    yf.store_raw(ry, a, 0);
-  };
-  // the later spans are read again, each one's loads issued before the previous span
-  // is written (a load past this workgroup's spans, or past the row, is harmless)
-  Own cur = first;
+    const rsrc_t ry = row_rsrc<SX>(p.y, p.ldy, row, N);
+    auto emit = [&](Own& in, int a) {
+      summed(in.x, in.r);
+      if constexpr (OP == OP_FADD) in.x.store_raw(row_rsrc<SX>(p.ro, p.ldro, row, N), a, 0);
+      float o[EVE];
+#pragma unroll
+      for (int i = 0; i < EVE; ++i) {
+        if constexpr (OP == OP_LN) {
+          const double e = static_cast<double>(in.x.get(i)) - mean;
+          o[i] = static_cast<float>(fma(e * rstd, static_cast<double>(in.w.get(i)),
+                                        static_cast<double>(in.b.get(i))));
+        } else {
+          o[i] = (in.x.get(i) * rs) * (in.w.get(i) + p.offset);
+        }
+      }
+      FX yf;
+      yf.pack(o);
+      yf.store_raw(ry, a, 0);
+    };
+    emit(first, s_first * SPLIT_WG + t);
+    if constexpr (MORE) {
+#pragma unroll
+      for (int k = 0; k < SPLIT_AHEAD; ++k) {
+        if (s_first + 1 + k < s_end) emit(ahead[k], (s_first + 1 + k) * SPLIT_WG + t);  // uniform
+      }
+      // any further spans, each one's loads issued before the previous span is written
+      const int s_more = s_first + 1 + SPLIT_AHEAD;
+      if (s_more < s_end) {
+        Own cur;
+        load_own(cur, s_more * SPLIT_WG + t);
 #pragma unroll 1
-  for (int sp = s_first; sp < s_end; ++sp) {
-    Own nxt;
-    load_own(nxt, (sp + 1) * SPLIT_WG + t);
-    emit(cur, sp * SPLIT_WG + t);
-    cur = nxt;
-  }
+        for (int sp = s_more; sp < s_end; ++sp) {
+          Own nxt;
+          load_own(nxt, (sp + 1) * SPLIT_WG + t);
+          emit(cur, sp * SPLIT_WG + t);
+          cur = nxt;
+        }
+      }
+    }
+  };
+  if (s_end - s_first > 1) finish(SplitMore<true>{});
+  else finish(SplitMore<false>{});
 }
 
 // Backward (stage 1).  grid = (workgroups per row, M).  pw / pb: row i of the partial
@@ -315,77 +348,101 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
 #pragma unroll
     for (int u = 1; u < SPLIT_U; ++u) acc[j] += part[u][j];
   }
-  team_sum<NA>(acc, SPLIT_WG / 64, 0, red, parity);
+  // Reduction and output.  A workgroup of several spans reads the next ones (loads past
+  // its spans or the row are harmless and unused) while the row's sums are reduced; a
+  // one-span workgroup (a decode row) issues no such loads.  The two are separate code
+  // paths, so neither waits for loads it does not use.
+  auto finish = [&](auto more) {
+    constexpr bool MORE = decltype(more)::value;
+    Own ahead[MORE ? SPLIT_AHEAD : 1];
+    if constexpr (MORE) {
+#pragma unroll
+      for (int k = 0; k < SPLIT_AHEAD; ++k) load_own(ahead[k], (s_first + 1 + k) * SPLIT_WG + t);
+    }
+    team_sum<NA>(acc, SPLIT_WG / 64, 0, red, parity);
 
-  // row constants: dx = rstd * g + c0 - x * cx (LN: c0 = -mean(g) * rstd and x taken
-  // as x - mean; RMS: c0 = 0); xhat = x * rs + nmr (nmr = 0 for RMS)
-  double rstd, cx, c0 = 0.0, mean = 0.0;
-  if constexpr (OP == OP_LN) {
-    acc[0] = fma(pad, K, acc[0]);  // slots past N: d = -K, g = 0
-    acc[1] = fma(-pad * K, K, acc[1]);
-    const double delta = acc[0] * inv_n;  // mean - K
-    const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
-    rstd = rsqrt_d(var + static_cast<double>(p.eps));
-    mean = K + delta;
-    const double mg = acc[2] * inv_n;                // mean(g)
-    const double mgd = acc[3] * inv_n - delta * mg;  // mean(g * (x - mean))
-    // dx = rstd * (g - mean(g) - (x - mean) * rstd^2 * mean(g * (x - mean)))
-    cx = mgd * rstd * rstd * rstd;
-    c0 = -mg * rstd;
-  } else {
-    rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
-    // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
-    cx = rstd * rstd * rstd * (acc[1] * inv_n);
-  }
-  const float rs = static_cast<float>(rstd);
-  const float nmr = static_cast<float>(-mean * rstd);
-  const rsrc_t rdx = row_rsrc<SX>(p.dx, p.lddx, row, N);
-  // a span's products go to partial row `row` as 16-byte groups (N is a multiple of
-  // EVE, so an access lies wholly inside the row or wholly past it, where stores vanish)
-  auto put = [&](float* dst, const float (&v)[EVE], int a) {
-    const rsrc_t rp = make_rsrc(dst + row * p.ldws, static_cast<uint32_t>(N) * 4u);
-#pragma unroll
-    for (int q = 0; q < EVE / 4; ++q) {
-      const v4u w4 = {__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
-                      __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
-      __builtin_amdgcn_raw_buffer_store_b128(w4, rp, (a * EVE + 4 * q) * 4, 0, 0);
+    // row constants: dx = rstd * g + c0 - x * cx (LN: c0 = -mean(g) * rstd and x taken
+    // as x - mean; RMS: c0 = 0); xhat = x * rs + nmr (nmr = 0 for RMS)
+    double rstd, cx, c0 = 0.0, mean = 0.0;
+    if constexpr (OP == OP_LN) {
+      acc[0] = fma(pad, K, acc[0]);  // slots past N: d = -K, g = 0
+      acc[1] = fma(-pad * K, K, acc[1]);
+      const double delta = acc[0] * inv_n;  // mean - K
+      const double var = fmax(acc[1] * inv_n - delta * delta, 0.0);
+      rstd = rsqrt_d(var + static_cast<double>(p.eps));
+      mean = K + delta;
+      const double mg = acc[2] * inv_n;                // mean(g)
+      const double mgd = acc[3] * inv_n - delta * mg;  // mean(g * (x - mean))
+      // dx = rstd * (g - mean(g) - (x - mean) * rstd^2 * mean(g * (x - mean)))
+      cx = mgd * rstd * rstd * rstd;
+      c0 = -mg * rstd;
+    } else {
+      rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
+      // dx = rstd * (g - xhat * mean(g * xhat)) = rstd * g - c * x, c = rstd^3 * mean(g * x)
+      cx = rstd * rstd * rstd * (acc[1] * inv_n);
     }
-  };
-  auto emit = [&](const Own& in, int a) {
-    float o[EVE], dwp[EVE], dbp[EVE];
+    const float rs = static_cast<float>(rstd);
+    const float nmr = static_cast<float>(-mean * rstd);
+    const rsrc_t rdx = row_rsrc<SX>(p.dx, p.lddx, row, N);
+    // a span's products go to partial row `row` as 16-byte groups (N is a multiple of
+    // EVE, so an access lies wholly inside the row or wholly past it, where stores vanish)
+    auto put = [&](float* dst, const float (&v)[EVE], int a) {
+      const rsrc_t rp = make_rsrc(dst + row * p.ldws, static_cast<uint32_t>(N) * 4u);
 #pragma unroll
-    for (int i = 0; i < EVE; ++i) {
-      const float xs = in.x.get(i);
-      const float dys = in.g.get(i);
-      const double g = gval(dys, in.w.get(i));
-      if constexpr (OP == OP_LN) {
-        const double e = static_cast<double>(xs) - mean;
-        o[i] = static_cast<float>(fma(-e, cx, fma(g, rstd, c0)));
-        dwp[i] = dys * fmaf(xs, rs, nmr);
-      } else {
-        double dxd = fma(-static_cast<double>(xs), cx, g * rstd);
-        if constexpr (OP == OP_FADD) dxd += static_cast<double>(in.d.get(i));
-        o[i] = static_cast<float>(dxd);
-        dwp[i] = dys * (xs * rs);
+      for (int q = 0; q < EVE / 4; ++q) {
+        const v4u w4 = {__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                        __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w4, rp, (a * EVE + 4 * q) * 4, 0, 0);
       }
-      dbp[i] = dys;
-    }
-    FX of;
-    of.pack(o);
-    of.store_raw(rdx, a, 0);
-    if constexpr (CDW) put(p.pw, dwp, a);
-    if constexpr (CDB) put(p.pb, dbp, a);
-  };
-  // the later spans are read again, each one's loads issued before the previous span
-  // is written (a load past this workgroup's spans, or past the row, is harmless)
-  Own cur = first;
+    };
+    auto emit = [&](const Own& in, int a) {
+      float o[EVE], dwp[EVE], dbp[EVE];
+#pragma unroll
+      for (int i = 0; i < EVE; ++i) {
+        const float xs = in.x.get(i);
+        const float dys = in.g.get(i);
+        const double g = gval(dys, in.w.get(i));
+        if constexpr (OP == OP_LN) {
+          const double e = static_cast<double>(xs) - mean;
+          o[i] = static_cast<float>(fma(-e, cx, fma(g, rstd, c0)));
+          dwp[i] = dys * fmaf(xs, rs, nmr);
+        } else {
+          double dxd = fma(-static_cast<double>(xs), cx, g * rstd);
+          if constexpr (OP == OP_FADD) dxd += static_cast<double>(in.d.get(i));
+          o[i] = static_cast<float>(dxd);
+          dwp[i] = dys * (xs * rs);
+        }
+        dbp[i] = dys;
+      }
+      FX of;
+      of.pack(o);
+      of.store_raw(rdx, a, 0);
+      if constexpr (CDW) put(p.pw, dwp, a);
+      if constexpr (CDB) put(p.pb, dbp, a);
+    };
+    emit(first, s_first * SPLIT_WG + t);
+    if constexpr (MORE) {
+#pragma unroll
+      for (int k = 0; k < SPLIT_AHEAD; ++k) {
+        if (s_first + 1 + k < s_end) emit(ahead[k], (s_first + 1 + k) * SPLIT_WG + t);  // uniform
+      }
+      // any further spans, each one's loads issued before the previous span is written
+      const int s_more = s_first + 1 + SPLIT_AHEAD;
+      if (s_more < s_end) {
+        Own cur;
+        load_own(cur, s_more * SPLIT_WG + t);
 #pragma unroll 1
-  for (int sp = s_first; sp < s_end; ++sp) {
-    Own nxt;
-    load_own(nxt, (sp + 1) * SPLIT_WG + t);
-    emit(cur, sp * SPLIT_WG + t);
-    cur = nxt;
-  }
+        for (int sp = s_more; sp < s_end; ++sp) {
+          Own nxt;
+          load_own(nxt, (sp + 1) * SPLIT_WG + t);
+          emit(cur, sp * SPLIT_WG + t);
+          cur = nxt;
+        }
+      }
+    }
+  };
+  if (s_end - s_first > 1) finish(SplitMore<true>{});
+  else finish(SplitMore<false>{});
 }
 
 }  // namespace rn
