@@ -10,10 +10,9 @@
 // workgroup of the row, so all of them hold bitwise-identical statistics and none
 // waits for another (the redundant reads hit L2); then it writes its own spans of the
 // outputs (the first one loaded before the walk, the next ones read again while the
-// row's sums are reduced).  The
-// arithmetic is the one of the row kernels (rn_kernels.h): fp64 sums, LayerNorm y and
-// every dx formed in fp64 and rounded once, RMSNorm y in fp32 with the offset added to
-// the weight in fp32 ([gemma], Summary).
+// row's sums are reduced).  The arithmetic is the one of the row kernels
+// (rn_kernels.h): fp64 sums, LayerNorm y and every dx formed in fp64 and rounded once,
+// RMSNorm y in fp32 with the offset added to the weight in fp32 ([gemma], Summary).
 //
 // Parameter gradients: row i's products dy * xhat (and dy) for the span are written to
 // partial row i, so the partial rows are the rows themselves (P = M) and the column
@@ -39,6 +38,7 @@ constexpr int SPLIT_U = RN_SPLIT_U;   // spans per batch of the statistics walk 
 // (their latency then overlaps the row reduction); any further ones one ahead of use.
 constexpr int SPLIT_AHEAD = RN_SPLIT_AHEAD;
 
+// Selects, at compile time, the output code path of a workgroup with more than one span.
 template <bool B> struct SplitMore { static constexpr bool value = B; };
 
 // Buffer resource over row `row` of a row tensor (N elements of SX).
