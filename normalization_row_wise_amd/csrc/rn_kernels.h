@@ -25,7 +25,8 @@
 // window of the tensor, instead of one slice per workgroup scattered over all of it
 // (measured faster at large M).  When a thread's share of the row tensors is small
 // enough (fwd_prefetch, bwd_prefetch), the next row's tensors are loaded into a second
-// register set before the current row is reduced (two rows in flight per team).
+// register set before the current row is reduced (two rows in flight per team; three
+// in the fused add's trainable backward, bwd_prefetch2).
 // Columns past N inside the team's span are loaded as zeros; LayerNorm's shifted sums
 // are corrected for them once per row.
 #pragma once
@@ -83,6 +84,16 @@ constexpr bool fwd_prefetch(int V, int B) { return lane_bytes(V, B) <= RN_FWD_PF
 // is for two, so a third tensor lowers it in proportion.
 constexpr bool bwd_prefetch(int V, int B, bool grads, int nin) {
   return lane_bytes(V, B) * nin <= 2 * (grads ? RN_BWD_PF_BYTES : RN_FROZEN_PF_BYTES);
+}
+// The fused add's backward with parameter gradients keeps two rows in flight ahead of
+// the one it reduces (three register sets).  Its three row tensors, read by at most one
+// workgroup per CU, leave too few bytes in flight with one row ahead (graph-replayed
+// fwd + bwd steps, bf16: 2048 x 8192 60.7 -> 58.4 us, 8192 x 4096 103.5 -> 101.1 us;
+// fp16 with an fp32 weight 4096 x 4096 58.4 -> 56.8 us).  The two-tensor kernels gained
+// nothing from it and some lost (LayerNorm fp32 4096 x 8192 137.6 -> 140.3 us, narrow
+// rows 3-4 % slower); at V = 32, and with element accesses, the third set spills.
+constexpr bool bwd_prefetch2(int op, int V, bool vec, bool prefetch, bool grads) {
+  return prefetch && grads && vec && op == OP_FADD && V <= 16;
 }
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
 // (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.
@@ -490,6 +501,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   constexpr int EVE = 16 / Ty<DX>::B;
   constexpr int NG = (CDW ? 1 : 0) + (CDB ? 1 : 0);
   constexpr bool PF = bwd_prefetch(V, Ty<DX>::B, NG > 0, OP == OP_FADD ? 3 : 2);
+  constexpr bool PF2 = bwd_prefetch2(OP, V, VEC, PF, NG > 0);
   using FX = Frag<DX, V, EVE, VEC>;
   using FW = Frag<DW, V, EVE, VEC>;
   using SX = typename Ty<DX>::S;
@@ -685,7 +697,22 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     frag_store<TS>(of, at(p.dx, p.lddx, it), t, T, N);
   };
 
-  if constexpr (PF) {
+  if constexpr (PF2) {
+    // as below, two rows ahead
+    In a, b, c;
+    load(a, 0);
+    load(b, 1);
+    for (int it = 0; it < iters; it += 3) {
+      load(c, it + 2);
+      process(a, it);
+      if (it + 1 >= iters) break;
+      load(a, it + 3);
+      process(b, it + 1);
+      if (it + 2 >= iters) break;
+      load(b, it + 4);
+      process(c, it + 2);
+    }
+  } else if constexpr (PF) {
     // The next row's loads are issued unconditionally (past the share they read
     // zeros): a load issued on one path only makes the wait before the current row's
     // data a full vmcnt(0), which also waits for the previous row's stores.
