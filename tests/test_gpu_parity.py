@@ -134,6 +134,31 @@ def test_frozen_dx_bit_identical_wide_and_fused(case):
     assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
 
 
+# The fused add's trainable backward walks its rows through a ring of three register
+# sets (two rows loaded ahead of the one reduced).  Row counts that give each team 3, 4
+# and 5 rows end the walk at each point of the ring; every row is checked, and dx must
+# still equal the frozen kernel's bit for bit.
+@pytest.mark.parametrize("case", [
+    (1531, 4096, "bf16", "bf16", True, True),     # two teams per workgroup, 3 rows each
+    (2043, 4096, "fp16", "fp32", False, True),    # 4 rows each
+    (2555, 4096, "bf16", "fp32", True, True),     # 5 rows each
+    (1279, 8192, "bf16", "bf16", True, False),    # one team per workgroup, 5 rows; no dres
+    (4000, 2048, "fp16", "fp16", False, True),    # four teams per workgroup, 4 rows each
+], ids=lambda c: f"{c[0]}x{c[1]}_{c[2]}_{c[3]}")
+def test_fused_add_row_ring(case):
+    m, n, io, wt, gemma, dres = case
+    wl = workloads.small("fused_add_rmsnorm", m, n, io, wt, offset=1.0 if gemma else 0.0,
+                         weight="gemma" if gemma else "unit", dres=dres, seed=13 + m)
+    _say("row ring", wl.name)
+    fails = gp.check(wl)
+    assert not fails, "\n".join(fails)
+    t = workloads.generate(wl)
+    full = gp.run_gpu(wl, t, dw=True, db=True)
+    frozen = gp.run_gpu(wl, t, dw=False, db=False)
+    bits = torch.int32 if io == "fp32" else torch.int16
+    assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
+
+
 @pytest.mark.parametrize("op", ["rmsnorm", "fused_add_rmsnorm"])
 def test_dw_independent_of_offset(op):
     # the offset is a constant of the weight: dw must not move with it
