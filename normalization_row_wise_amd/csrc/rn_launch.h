@@ -17,6 +17,7 @@ struct Launch {
   size_t shmem;   // dynamic LDS bytes
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;  // optional kernel timing
   bool split = false;  // rows spread over workgroups (rn_split.h; v, ts unused)
+  bool group = false;  // split: a row's workgroups renumbered onto one XCD
 };
 
 // Launch through hipExtLaunchKernel when timing events are attached.
@@ -54,7 +55,8 @@ template <int OP, int DX, int DW>
 inline bool fwd_v(const Launch& l, const FwdArgs& a, hipStream_t s) {
   if (l.split) {
     if (!l.vec) return false;
-    launch_kernel(split_fwd_kernel<OP, DX, DW>, l, s, a);
+    launch_kernel(l.group ? split_fwd_kernel<OP, DX, DW, true> : split_fwd_kernel<OP, DX, DW, false>,
+                  l, s, a);
     return true;
   }
   if (l.ts != 0) {  // sub-wave teams: V = 8, 16-byte accesses
@@ -131,11 +133,15 @@ inline bool bwd_flags(const BwdVariant& b, const Launch& l, const BwdArgs& a, hi
     if (!l.vec) return false;
     if constexpr (can_xg) {
       if (b.xg) {
-        launch_kernel(split_bwd_kernel<OP, DX, DW, CDW, CDB, true>, l, s, a);
+        launch_kernel(l.group ? split_bwd_kernel<OP, DX, DW, CDW, CDB, true, true>
+                              : split_bwd_kernel<OP, DX, DW, CDW, CDB, true, false>,
+                      l, s, a);
         return true;
       }
     }
-    launch_kernel(split_bwd_kernel<OP, DX, DW, CDW, CDB, false>, l, s, a);
+    launch_kernel(l.group ? split_bwd_kernel<OP, DX, DW, CDW, CDB, false, true>
+                          : split_bwd_kernel<OP, DX, DW, CDW, CDB, false, false>,
+                  l, s, a);
     return true;
   }
   if constexpr (!CDW && !CDB) {

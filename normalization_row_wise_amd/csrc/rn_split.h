@@ -8,9 +8,11 @@
 // the `spans_per_wg` consecutive spans from c * spans_per_wg of row i.  It first walks
 // the whole row and forms the row's sums itself, in the same order as every other
 // workgroup of the row, so all of them hold bitwise-identical statistics and none
-// waits for another (the redundant reads hit L2); then it writes its own spans of the
-// outputs (the first one loaded before the walk, the next ones read again while the
-// row's sums are reduced).  The arithmetic is the one of the row kernels
+// waits for another.  The redundant reads come from the caches: the L2 for workgroups
+// on one XCD, else the memory-side cache (when that would move many bytes across XCDs,
+// a row's workgroups are renumbered onto one XCD: split_pos).  Then it writes its own
+// spans of the outputs (the first one loaded before the walk, the next ones read again
+// while the row's sums are reduced).  The arithmetic is the one of the row kernels
 // (rn_kernels.h): fp64 sums, LayerNorm y and every dx formed in fp64 and rounded once,
 // RMSNorm y in fp32 with the offset added to the weight in fp32 ([gemma], Summary).
 //
@@ -53,8 +55,28 @@ template <int DX> __device__ __forceinline__ int spans_of(int N) {
   return (N + S - 1) / S;
 }
 
+// Logical (span group c, row) of workgroup (blockIdx.x, blockIdx.y).  Workgroups are
+// dealt to the 8 XCDs round-robin by linear id, so the workgroups of one row land on
+// different XCDs and each fetches the row for its walk into its own L2.  GROUP renumbers
+// them so that each XCD takes a contiguous block of logical ids: a row's workgroups then
+// share one L2 and the row crosses to that XCD once.  A bijection for any grid.
+template <bool GROUP> __device__ __forceinline__ void split_pos(int& c, int64_t& row) {
+  if constexpr (!GROUP) {
+    c = blockIdx.x;
+    row = blockIdx.y;
+  } else {
+    const int W = gridDim.x * gridDim.y;
+    const int k = blockIdx.y * gridDim.x + blockIdx.x;
+    const int x = k & 7, slot = k >> 3;
+    const int q = W >> 3, r = W & 7;  // XCDs below r take q + 1 workgroups, the others q
+    const int L = x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+    c = L % gridDim.x;
+    row = L / gridDim.x;
+  }
+}
+
 // Forward.  grid = (workgroups per row, M).
-template <int OP, int DX, int DW>
+template <int OP, int DX, int DW, bool GROUP>
 __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
   using FX = Frag<DX, EVE, EVE, true>;
@@ -64,10 +86,12 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
   __shared__ double red[2][16][4];
   int parity = 0;
   const int t = threadIdx.x;
-  const int64_t row = blockIdx.y;
+  int c;
+  int64_t row;
+  split_pos<GROUP>(c, row);
   const int N = p.N;
   const int NS = spans_of<DX>(N);
-  const int s_first = blockIdx.x * p.spans_per_wg;
+  const int s_first = c * p.spans_per_wg;
   const int s_end = min(s_first + p.spans_per_wg, NS);
   const double inv_n = 1.0 / N;
   const double pad = static_cast<double>(NS) * SPLIT_WG * EVE - N;
@@ -181,7 +205,7 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
       rstd = rsqrt_d(acc[0] * inv_n + static_cast<double>(p.eps));
     }
     const float rs = static_cast<float>(rstd);
-    if (blockIdx.x == 0 && t == 0) {
+    if (c == 0 && t == 0) {
       if (p.rstd != nullptr) p.rstd[row] = rs;
       if constexpr (OP == OP_LN) {
         if (p.mean != nullptr) p.mean[row] = static_cast<float>(mean);
@@ -233,7 +257,7 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
 
 // Backward (stage 1).  grid = (workgroups per row, M).  pw / pb: row i of the partial
 // rows (stride ldws), or dw / db themselves when M = 1.
-template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG>
+template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG, bool GROUP>
 __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
   using FX = Frag<DX, EVE, EVE, true>;
@@ -245,10 +269,12 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
   __shared__ double red[2][16][4];
   int parity = 0;
   const int t = threadIdx.x;
-  const int64_t row = blockIdx.y;
+  int c;
+  int64_t row;
+  split_pos<GROUP>(c, row);
   const int N = p.N;
   const int NS = spans_of<DX>(N);
-  const int s_first = blockIdx.x * p.spans_per_wg;
+  const int s_first = c * p.spans_per_wg;
   const int s_end = min(s_first + p.spans_per_wg, NS);
   const double inv_n = 1.0 / N;
   const double pad = static_cast<double>(NS) * SPLIT_WG * EVE - N;

@@ -63,6 +63,13 @@ CASES = [
     _wl("layernorm", 7, 1028, "fp32"),                   # spans of 1024 + 4
     _wl("rmsnorm", 3, 2056, "fp16", "fp32", gemma=True),  # spans of 2048 + 8
     _wl("fused_add_rmsnorm", 128, 4104, "fp16", gemma=True),  # 2 of 2 / 1 spans
+    # Rows whose walks would fetch many bytes across XCDs: their workgroups are
+    # renumbered onto one XCD per row (grid sizes 161, 117, 110 and 252: not multiples
+    # of the 8 XCDs, so some XCDs take one workgroup more than others)
+    _wl("rmsnorm", 7, 23552, "fp32"),                    # 23 workgroups of 1 span
+    _wl("fused_add_rmsnorm", 13, 18432, "bf16", gemma=True),  # 9 of 1 span
+    _wl("fused_add_rmsnorm", 11, 18440, "fp16", "fp32"),  # 10 of 1, ragged last span
+    _wl("layernorm", 21, 24568, "bf16"),                  # 12 of 1, ragged last span
 ]
 
 
