@@ -103,6 +103,8 @@ GRAPH_CASES = [
     # split rows (a decode row; a small LayerNorm batch): several workgroups per row
     workloads.small("rmsnorm", 1, 18432, "bf16", "fp32", seed=35),
     workloads.small("layernorm", 3, 8192, "bf16", seed=36),
+    # split rows whose workgroups are renumbered onto one XCD per row
+    workloads.small("fused_add_rmsnorm", 32, 16384, "bf16", offset=1.0, weight="gemma", seed=37),
 ]
 
 
