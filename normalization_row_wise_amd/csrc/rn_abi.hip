@@ -295,6 +295,7 @@ inline Split split_plan(int kind, int op, int64_t M, int64_t N, int eb, bool vec
   Split sp;
   const Override& o = g_override[kind];
   if (!vec || aliased || o.v || o.rows || o.wg_rows) return sp;
+  if (M > max_partials(N)) return sp;  // one partial row per row must fit the workspace
   const int64_t ns = cdiv(N, static_cast<int64_t>(SPLIT_WG) * (16 / eb));
   const int64_t g = std::min<int64_t>(ns, RN_SPLIT_MAX_WG / M);
   if (g < 2) return sp;
