@@ -134,6 +134,47 @@ def test_frozen_dx_bit_identical_wide_and_fused(case):
     assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
 
 
+# Wide 16-bit rows whose trainable backward also loads one row ahead: RMSNorm and
+# LayerNorm at 48 elements per lane with exact fp32 products (16-bit weight, no
+# offset), and the fused add at 32 elements per lane.  Rows past 128 take the row
+# kernels; the row counts give workgroups an odd and an even number of rows.  LayerNorm
+# at this width with both gradients keeps its accumulators in registers and does not
+# prefetch, so it is run with the bias frozen (dW only) and with the weight frozen.
+WIDE_PF = [
+    workloads.small("rmsnorm", 1001, 18432, "bf16", seed=81),           # V = 48
+    workloads.small("rmsnorm", 517, 20480, "fp16", seed=82),            # V = 48
+    workloads.small("fused_add_rmsnorm", 700, 12288, "bf16", offset=1.0, weight="gemma",
+                    seed=83),                                           # V = 32
+    workloads.small("fused_add_rmsnorm", 1290, 16384, "fp16", "fp32", dres=False, seed=84),
+]
+
+
+@pytest.mark.parametrize("wl", WIDE_PF, ids=lambda c: c.name)
+def test_wide_rows_one_row_ahead(wl):
+    _say("wide prefetch", wl.name)
+    fails = gp.check(wl, sample_rows=512)
+    assert not fails, "\n".join(fails)
+    t = workloads.generate(wl)
+    full = gp.run_gpu(wl, t, dw=True, db=True)
+    frozen = gp.run_gpu(wl, t, dw=False, db=False)
+    assert torch.equal(full["dx"].view(torch.int16), frozen["dx"].view(torch.int16))
+
+
+@pytest.mark.parametrize("grad", ["dw", "db"])
+def test_wide_layernorm_one_gradient(grad):
+    wl = workloads.small("layernorm", 300, 18432, "bf16", seed=85)
+    _say("wide layernorm", grad, wl.name)
+    t = workloads.generate(wl)
+    g = gp.run_gpu(wl, t, dw=grad == "dw", db=grad == "db")
+    o = gp.run_oracle(wl, t)
+    rep = gp.io_report(g["dx"].cpu(), o["dx"], wl.io)
+    assert gp.io_ok(rep, wl.io), rep
+    assert gp.f32_report(g[grad].cpu(), o[grad]) <= gp.REL_GRAD
+    other = "db" if grad == "dw" else "dw"
+    assert g[other] is None
+    frozen = gp.run_gpu(wl, t, dw=False, db=False)
+    assert torch.equal(g["dx"].view(torch.int16), frozen["dx"].view(torch.int16))
+
 # The fused add's trainable backward walks its rows through a ring of three register
 # sets (two rows loaded ahead of the one reduced).  Row counts that give each team 3, 4
 # and 5 rows end the walk at each point of the ring; every row is checked, and dx must
