@@ -97,14 +97,14 @@ constexpr bool bwd_prefetch2(int op, int V, bool vec, bool prefetch, bool grads)
 }
 // Wider shares of 16-bit rows that still take one row ahead in a trainable backward
 // with LDS accumulators: the fused add at V = 32, and RMSNorm / LayerNorm at V = 48
-// with exact fp32 products (no fp32 weight copy to widen).  Their instances keep the
-// second register set within 256 VGPRs without spilling; the others at these widths
-// spill and ran 45-60 % slower with it.  Graph-replayed fwd + bwd steps, trainable,
-// us: RMSNorm 4096 x 18432 bf16 171.6 -> 158.5, fp16 2048 x 20480 101.5 -> 93.3, fused
-// add 2048 x 12288 bf16 90.6 -> 86.7, 2048 x 16384 bf16 Gemma 120.7 -> 115.9.
-constexpr bool bwd_prefetch_wide(int op, int V, int B, bool vec, bool xg, int acc, bool grads) {
+// with a 16-bit weight (WB = 2).  Their instances keep the second register set within
+// 256 VGPRs without spilling; with an fp32 weight they spill and ran 45-60 % slower.
+// Graph-replayed fwd + bwd steps, trainable, us: RMSNorm 4096 x 18432 bf16 171.6 ->
+// 158.5, fp16 2048 x 20480 101.5 -> 93.3, fused add 2048 x 12288 bf16 90.6 -> 86.7,
+// 2048 x 16384 bf16 Gemma 120.7 -> 115.9.
+constexpr bool bwd_prefetch_wide(int op, int V, int B, int WB, bool vec, int acc, bool grads) {
   return grads && vec && acc == 1 && B == 2 &&
-         ((op == OP_FADD && V == 32) || (op != OP_FADD && V == 48 && xg));
+         ((op == OP_FADD && V == 32) || (op != OP_FADD && V == 48 && WB == 2));
 }
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
 // (128 VGPRs per lane) for small per-lane shares, 8 waves (256 VGPRs) above.
@@ -511,7 +511,7 @@ template <int OP, int DX, int DW, int V, bool VEC, bool CDW, bool CDB, bool XG, 
 __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p) {
   constexpr int EVE = 16 / Ty<DX>::B;
   constexpr int NG = (CDW ? 1 : 0) + (CDB ? 1 : 0);
-  constexpr bool PF = (TS == 0 && bwd_prefetch_wide(OP, V, Ty<DX>::B, VEC, XG, ACC, NG > 0)) ||
+  constexpr bool PF = (TS == 0 && bwd_prefetch_wide(OP, V, Ty<DX>::B, Ty<DW>::B, VEC, ACC, NG > 0)) ||
                       bwd_prefetch(V, Ty<DX>::B, NG > 0, OP == OP_FADD ? 3 : 2);
   constexpr bool PF2 = bwd_prefetch2(OP, V, VEC, PF, NG > 0);
   using FX = Frag<DX, V, EVE, VEC>;
@@ -538,8 +538,10 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   // The weight of this thread's columns.  Frozen instances keep it as loaded (16-bit
   // words unpacked on use: half the VGPRs of an fp32 copy, so more waves per SIMD); the
   // trainable ones, whose extra dW work makes them short of VALU issue rather than of
-  // waves, keep an fp32 copy and save the unpacking.
-  constexpr bool PACKW = NG == 0;
+  // waves, keep an fp32 copy and save the unpacking, except at V = 48 with a 16-bit
+  // weight and an fp64 weight path (an offset): there the copy made them spill
+  // (RMSNorm 4096 x 18432 bf16 Gemma trainable step 187.1 -> 164.4 us kept packed).
+  constexpr bool PACKW = NG == 0 || (V >= 48 && Ty<DW>::B == 2 && !XG);
   // The same budget argument for the row itself: a trainable launch of whole-wave
   // teams has at most one workgroup per CU (one partial row each, at most 256 of them),
   // so it can keep what the statistics pass derived from dy (V <= 32) and x (V <= 16)

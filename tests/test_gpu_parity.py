@@ -135,14 +135,20 @@ def test_frozen_dx_bit_identical_wide_and_fused(case):
 
 
 # Wide 16-bit rows whose trainable backward also loads one row ahead: RMSNorm and
-# LayerNorm at 48 elements per lane with exact fp32 products (16-bit weight, no
-# offset), and the fused add at 32 elements per lane.  Rows past 128 take the row
-# kernels; the row counts give workgroups an odd and an even number of rows.  LayerNorm
-# at this width with both gradients keeps its accumulators in registers and does not
-# prefetch, so it is run with the bias frozen (dW only) and with the weight frozen.
+# LayerNorm at 48 elements per lane with a 16-bit weight (exact fp32 products, or with
+# a Gemma offset the weight kept packed), and the fused add at 32 elements per lane (at
+# 48 it keeps a Gemma weight packed but loads one row at a time).  Rows past 128 take
+# the row kernels; the row counts give workgroups an odd and an even number of rows.
+# LayerNorm at this width with both gradients keeps its accumulators in registers and
+# does not prefetch, so it is run with the bias frozen (dW only) and with the weight
+# frozen.
 WIDE_PF = [
     workloads.small("rmsnorm", 1001, 18432, "bf16", seed=81),           # V = 48
     workloads.small("rmsnorm", 517, 20480, "fp16", seed=82),            # V = 48
+    workloads.small("rmsnorm", 900, 18432, "bf16", offset=1.0, weight="gemma", seed=86),
+    workloads.small("rmsnorm", 300, 24576, "fp16", offset=1.0, weight="gemma", seed=87),
+    workloads.small("fused_add_rmsnorm", 600, 18432, "bf16", offset=1.0, weight="gemma",
+                    seed=88),                                           # V = 48
     workloads.small("fused_add_rmsnorm", 700, 12288, "bf16", offset=1.0, weight="gemma",
                     seed=83),                                           # V = 32
     workloads.small("fused_add_rmsnorm", 1290, 16384, "fp16", "fp32", dres=False, seed=84),
