@@ -163,7 +163,8 @@ struct Shape {
   int64_t grid = 0;
   int P = 0;               // partial rows (backward with grads)
   size_t shmem = 0;
-  int acc = 0;             // backward with grads: accumulators in LDS (1) or VGPRs (0)
+  int acc = 0;             // backward with grads: accumulators in LDS (1; 2: stride 384)
+                           // or VGPRs (0)
 };
 
 // Workgroups a forward launch aims for: enough to fill every CU many times over; at
@@ -221,11 +222,17 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
   if (kind == 1) {
     // LDS accumulators: one [V][wg_cap] fp32 block per gradient, whatever R is
     const size_t block = static_cast<size_t>(ngrads) * s.v * wg_cap * sizeof(float);
+    // both LayerNorm gradients at V = 48: blocks of stride 384 when the team fits in it
+    const size_t block48 = static_cast<size_t>(ngrads) * s.v * kAccS48 * sizeof(float);
     if (block <= kLdsBudget) {
       s.acc = 1;
       R = o.rows ? o.rows : r_cap;
       R = std::max(1, std::min(R, r_cap));
       s.shmem = block;
+    } else if (s.v == 48 && ngrads == 2 && vec && s.team <= kAccS48 && block48 <= kLdsBudget) {
+      s.acc = 2;
+      R = 1;
+      s.shmem = block48;
     } else {
       // accumulators in VGPRs; LDS only for the final team combine
       s.acc = 0;

@@ -103,7 +103,7 @@ constexpr bool bwd_prefetch2(int op, int V, bool vec, bool prefetch, bool grads)
 // 158.5, fp16 2048 x 20480 101.5 -> 93.3, fused add 2048 x 12288 bf16 90.6 -> 86.7,
 // 2048 x 16384 bf16 Gemma 120.7 -> 115.9.
 constexpr bool bwd_prefetch_wide(int op, int V, int B, int WB, bool vec, int acc, bool grads) {
-  return grads && vec && acc == 1 && B == 2 &&
+  return grads && vec && acc >= 1 && B == 2 &&
          ((op == OP_FADD && V == 32) || (op != OP_FADD && V == 48 && WB == 2));
 }
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
@@ -114,6 +114,8 @@ constexpr int fwd_max_wg(int V, int B) {
 constexpr int bwd_max_wg(int V, int B) {
   return lane_bytes(V, B) <= RN_BWD_BIG_WG_BYTES ? 1024 : 512;
 }
+// LDS accumulator stride of the ACC = 2 instances (V = 48, one team of <= 384 threads).
+constexpr int kAccS48 = 384;
 
 // The row's first element (0 for a zero-byte resource).
 template <int DX> __device__ __forceinline__ double first_elem(rsrc_t rs) {
@@ -345,6 +347,9 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
 //            and j * S * 16 is an immediate offset from one base register, so the
 //            compiler sees that the groups do not overlap and can overlap their reads.
 //            Only this thread touches its float4s: deterministic sums.
+//   ACC = 2: as ACC = 1 with S = kAccS48 (V = 48 with teams of at most 384 threads):
+//            both LayerNorm gradients' blocks then fit (144 KiB) where two blocks of
+//            stride 512 (192 KiB) would not.
 // Both add with one rounding: acc = fma(a, b, acc).
 template <int V, int ACC, int S> struct Acc {
   static_assert(V % 4 == 0, "accumulators are kept in groups of four");
@@ -520,6 +525,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   static_assert(!(CDB && OP != OP_LN), "only LayerNorm has a bias");
   static_assert(!(XG && Ty<DW>::B != 2), "exact fp32 products need a 16-bit weight");
   static_assert(NG > 0 || ACC == 0, "accumulators only exist with parameter gradients");
+  static_assert(ACC != 2 || (V == 48 && TS == 0), "the 384-stride blocks are for V = 48");
   __shared__ double red[2][16][4];
   extern __shared__ float part[];
   int parity = 0;
@@ -568,8 +574,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
     else if (!after_reduction) opaque<V>(wv);
   };
   // LDS accumulator blocks: [gradient][V/4][S][4]
-  constexpr int S = bwd_max_wg(V, Ty<DX>::B);
-  Acc<V, ACC, S> accw, accb;
+  constexpr int S = ACC == 2 ? kAccS48 : bwd_max_wg(V, Ty<DX>::B);
+  Acc<V, ACC == 2 ? 1 : ACC, S> accw, accb;
   if constexpr (CDW) accw.init(part, tid);
   if constexpr (CDB) accb.init(part + (CDW ? V * S : 0), tid);
 
@@ -749,7 +755,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
 
   float* const dst_w = CDW ? p.pw + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
   float* const dst_b = CDB ? p.pb + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
-  if constexpr (NG > 0 && ACC == 1) {
+  if constexpr (NG > 0 && ACC >= 1) {
     __syncthreads();  // every accumulation has landed
     if constexpr (CDW && CDB) {
       float* const dsts[2] = {dst_w, dst_b};

@@ -139,9 +139,9 @@ def test_frozen_dx_bit_identical_wide_and_fused(case):
 # a Gemma offset the weight kept packed), and the fused add at 32 elements per lane (at
 # 48 it keeps a Gemma weight packed but loads one row at a time).  Rows past 128 take
 # the row kernels; the row counts give workgroups an odd and an even number of rows.
-# LayerNorm at this width with both gradients keeps its accumulators in registers and
-# does not prefetch, so it is run with the bias frozen (dW only) and with the weight
-# frozen.
+# LayerNorm at this width also runs with the bias frozen (dW only) and with the weight
+# frozen; with both gradients its two LDS blocks fit at stride 384 (teams of at most 384
+# threads), wider teams keep the accumulators in registers.
 WIDE_PF = [
     workloads.small("rmsnorm", 1001, 18432, "bf16", seed=81),           # V = 48
     workloads.small("rmsnorm", 517, 20480, "fp16", seed=82),            # V = 48
@@ -152,6 +152,11 @@ WIDE_PF = [
     workloads.small("fused_add_rmsnorm", 700, 12288, "bf16", offset=1.0, weight="gemma",
                     seed=83),                                           # V = 32
     workloads.small("fused_add_rmsnorm", 1290, 16384, "fp16", "fp32", dres=False, seed=84),
+    # LayerNorm with both gradients at V = 48 and teams of 384 threads: both LDS
+    # accumulator blocks at stride 384
+    workloads.small("layernorm", 700, 18432, "bf16", seed=89),
+    workloads.small("layernorm", 300, 17408, "fp32", seed=90),
+    workloads.small("layernorm", 521, 18000, "fp16", "fp32", seed=91),
 ]
 
 
@@ -163,7 +168,8 @@ def test_wide_rows_one_row_ahead(wl):
     t = workloads.generate(wl)
     full = gp.run_gpu(wl, t, dw=True, db=True)
     frozen = gp.run_gpu(wl, t, dw=False, db=False)
-    assert torch.equal(full["dx"].view(torch.int16), frozen["dx"].view(torch.int16))
+    bits = torch.int32 if wl.io == "fp32" else torch.int16
+    assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
 
 
 @pytest.mark.parametrize("grad", ["dw", "db"])
