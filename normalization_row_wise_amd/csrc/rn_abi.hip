@@ -163,8 +163,8 @@ struct Shape {
   int64_t grid = 0;
   int P = 0;               // partial rows (backward with grads)
   size_t shmem = 0;
-  int acc = 0;             // backward with grads: accumulators in LDS (1; 2: stride 384)
-                           // or VGPRs (0)
+  int acc = 0;             // backward with grads: accumulators in LDS (1; 2: stride 384),
+                           // dW in LDS and dB in VGPRs (3), or both in VGPRs (0)
 };
 
 // Workgroups a forward launch aims for: enough to fill every CU many times over; at
@@ -233,6 +233,12 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
       s.acc = 2;
       R = 1;
       s.shmem = block48;
+    } else if (s.v == 48 && ngrads == 2 && vec && block / 2 <= kLdsBudget) {
+      // wider teams: dW's block in LDS, dB's accumulators in VGPRs
+      s.acc = 3;
+      R = o.rows ? o.rows : r_cap;
+      R = std::max(1, std::min(R, r_cap));
+      s.shmem = block / 2;
     } else {
       // accumulators in VGPRs; LDS only for the final team combine
       s.acc = 0;

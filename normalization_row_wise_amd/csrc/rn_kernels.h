@@ -96,14 +96,14 @@ constexpr bool bwd_prefetch2(int op, int V, bool vec, bool prefetch, bool grads)
   return prefetch && grads && vec && op == OP_FADD && V <= 16;
 }
 // Wider shares of 16-bit rows that still take one row ahead in a trainable backward
-// with LDS accumulators: the fused add at V = 32, and RMSNorm / LayerNorm at V = 48
+// with all accumulators in LDS: the fused add at V = 32, and RMSNorm / LayerNorm at V = 48
 // with a 16-bit weight (WB = 2).  Their instances keep the second register set within
 // 256 VGPRs without spilling; with an fp32 weight they spill and ran 45-60 % slower.
 // Graph-replayed fwd + bwd steps, trainable, us: RMSNorm 4096 x 18432 bf16 171.6 ->
 // 158.5, fp16 2048 x 20480 101.5 -> 93.3, fused add 2048 x 12288 bf16 90.6 -> 86.7,
 // 2048 x 16384 bf16 Gemma 120.7 -> 115.9.
 constexpr bool bwd_prefetch_wide(int op, int V, int B, int WB, bool vec, int acc, bool grads) {
-  return grads && vec && acc >= 1 && B == 2 &&
+  return grads && vec && (acc == 1 || acc == 2) && B == 2 &&
          ((op == OP_FADD && V == 32) || (op != OP_FADD && V == 48 && WB == 2));
 }
 // Largest workgroup a kernel is compiled for (sets its VGPR budget): 16 waves
@@ -350,6 +350,8 @@ __global__ __launch_bounds__(fwd_max_wg(V, Ty<DX>::B)) void fwd_kernel(FwdArgs p
 //   ACC = 2: as ACC = 1 with S = kAccS48 (V = 48 with teams of at most 384 threads):
 //            both LayerNorm gradients' blocks then fit (144 KiB) where two blocks of
 //            stride 512 (192 KiB) would not.
+//   ACC = 3: both LayerNorm gradients at V = 48 with wider teams: dW in LDS as for
+//            ACC = 1, dB in registers.
 // Both add with one rounding: acc = fma(a, b, acc).
 template <int V, int ACC, int S> struct Acc {
   static_assert(V % 4 == 0, "accumulators are kept in groups of four");
@@ -526,6 +528,7 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   static_assert(!(XG && Ty<DW>::B != 2), "exact fp32 products need a 16-bit weight");
   static_assert(NG > 0 || ACC == 0, "accumulators only exist with parameter gradients");
   static_assert(ACC != 2 || (V == 48 && TS == 0), "the 384-stride blocks are for V = 48");
+  static_assert(ACC != 3 || (CDW && CDB && TS == 0), "split homes are for dW and dB");
   __shared__ double red[2][16][4];
   extern __shared__ float part[];
   int parity = 0;
@@ -575,7 +578,8 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   };
   // LDS accumulator blocks: [gradient][V/4][S][4]
   constexpr int S = ACC == 2 ? kAccS48 : bwd_max_wg(V, Ty<DX>::B);
-  Acc<V, ACC == 2 ? 1 : ACC, S> accw, accb;
+  Acc<V, ACC >= 1 ? 1 : 0, S> accw;
+  Acc<V, ACC == 1 || ACC == 2 ? 1 : 0, S> accb;
   if constexpr (CDW) accw.init(part, tid);
   if constexpr (CDB) accb.init(part + (CDW ? V * S : 0), tid);
 
@@ -755,7 +759,13 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
 
   float* const dst_w = CDW ? p.pw + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
   float* const dst_b = CDB ? p.pb + static_cast<int64_t>(blockIdx.x) * p.ldws : nullptr;
-  if constexpr (NG > 0 && ACC >= 1) {
+  if constexpr (ACC == 3) {
+    __syncthreads();  // every accumulation has landed
+    float* const dsts[1] = {dst_w};
+    combine_lds<V, VEC, EVE, DX, S, 1>(part, dsts, R, T, N);
+    __syncthreads();  // `part` is reused by the register combine when R > 1
+    combine_regs<V, VEC, EVE, DX, S>(accb, dst_b, part, r, R, t, T, N);
+  } else if constexpr (NG > 0 && ACC >= 1) {
     __syncthreads();  // every accumulation has landed
     if constexpr (CDW && CDB) {
       float* const dsts[2] = {dst_w, dst_b};

@@ -35,7 +35,8 @@ bool launch_fwd_ln(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_
 bool launch_fwd_fadd(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s);
 // Backward variants: xg = exact fp32 product g = dy * w (16-bit weight, no offset);
 // acc = 1 keeps the dw / db accumulators in LDS, 2 in LDS blocks of stride 384 (V = 48,
-// both LayerNorm gradients), 0 in registers (V = 48 only).
+// both LayerNorm gradients), 3 dw in LDS and db in registers (V = 48, both LayerNorm
+// gradients, wider teams), 0 both in registers (V = 48 only).
 struct BwdVariant {
   bool cdw, cdb, xg;
   int acc;
@@ -96,12 +97,13 @@ inline bool bwd_one(const Launch& l, const BwdArgs& a, hipStream_t s) {
   if constexpr (ACC == 0 && (CDW || CDB) && V < 48) {
     // up to V = 32 the LDS accumulator blocks always fit
     return false;
-  } else if constexpr (ACC == 2 && !(V == 48 && CDW && CDB)) {
-    // the 384-stride blocks only serve both LayerNorm gradients at V = 48
+  } else if constexpr (ACC >= 2 && !(V == 48 && CDW && CDB)) {
+    // the 384-stride blocks and the split homes only serve both LayerNorm gradients at
+    // V = 48
     return false;
-  } else if constexpr (ACC == 2) {
+  } else if constexpr (ACC >= 2) {
     if (l.ts != 0 || !l.vec) return false;
-    return bwd_go(bwd_kernel<OP, DX, DW, V, true, CDW, CDB, XG, 2>, l, a, s);
+    return bwd_go(bwd_kernel<OP, DX, DW, V, true, CDW, CDB, XG, ACC>, l, a, s);
   } else {
     if constexpr (V == 8 && (ACC == 1 || (!CDW && !CDB))) {
       if (l.ts != 0) {  // sub-wave teams: V = 8, 16-byte accesses
@@ -132,6 +134,17 @@ inline bool bwd_v(const Launch& l, const BwdArgs& a, hipStream_t s) {
   }
 }
 
+template <int OP, int DX, int DW, bool CDW, bool CDB, bool XG>
+inline bool bwd_acc(int acc, const Launch& l, const BwdArgs& a, hipStream_t s) {
+  switch (acc) {
+    case 0: return bwd_v<OP, DX, DW, CDW, CDB, XG, 0>(l, a, s);
+    case 1: return bwd_v<OP, DX, DW, CDW, CDB, XG, 1>(l, a, s);
+    case 2: return bwd_v<OP, DX, DW, CDW, CDB, XG, 2>(l, a, s);
+    case 3: return bwd_v<OP, DX, DW, CDW, CDB, XG, 3>(l, a, s);
+    default: return false;
+  }
+}
+
 // Dispatch over the gradient flags, the exact-product path and the accumulator home.
 template <int OP, int DX, int DW, bool CDW, bool CDB>
 inline bool bwd_flags(const BwdVariant& b, const Launch& l, const BwdArgs& a, hipStream_t s) {
@@ -158,15 +171,9 @@ inline bool bwd_flags(const BwdVariant& b, const Launch& l, const BwdArgs& a, hi
     return bwd_v<OP, DX, DW, false, false, false, 0>(l, a, s);
   } else {
     if constexpr (can_xg) {
-      if (b.xg) {
-        if (b.acc == 2) return bwd_v<OP, DX, DW, CDW, CDB, true, 2>(l, a, s);
-        return b.acc ? bwd_v<OP, DX, DW, CDW, CDB, true, 1>(l, a, s)
-                     : bwd_v<OP, DX, DW, CDW, CDB, true, 0>(l, a, s);
-      }
+      if (b.xg) return bwd_acc<OP, DX, DW, CDW, CDB, true>(b.acc, l, a, s);
     }
-    if (b.acc == 2) return bwd_v<OP, DX, DW, CDW, CDB, false, 2>(l, a, s);
-    return b.acc ? bwd_v<OP, DX, DW, CDW, CDB, false, 1>(l, a, s)
-                 : bwd_v<OP, DX, DW, CDW, CDB, false, 0>(l, a, s);
+    return bwd_acc<OP, DX, DW, CDW, CDB, false>(b.acc, l, a, s);
   }
 }
 

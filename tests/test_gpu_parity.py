@@ -141,7 +141,7 @@ def test_frozen_dx_bit_identical_wide_and_fused(case):
 # the row kernels; the row counts give workgroups an odd and an even number of rows.
 # LayerNorm at this width also runs with the bias frozen (dW only) and with the weight
 # frozen; with both gradients its two LDS blocks fit at stride 384 (teams of at most 384
-# threads), wider teams keep the accumulators in registers.
+# threads), wider teams keep dW's in LDS and dB's in registers.
 WIDE_PF = [
     workloads.small("rmsnorm", 1001, 18432, "bf16", seed=81),           # V = 48
     workloads.small("rmsnorm", 517, 20480, "fp16", seed=82),            # V = 48
@@ -157,6 +157,10 @@ WIDE_PF = [
     workloads.small("layernorm", 700, 18432, "bf16", seed=89),
     workloads.small("layernorm", 300, 17408, "fp32", seed=90),
     workloads.small("layernorm", 521, 18000, "fp16", "fp32", seed=91),
+    # ... and with wider teams: dW's block in LDS, dB's accumulators in VGPRs
+    workloads.small("layernorm", 257, 20480, "fp16", seed=92),
+    workloads.small("layernorm", 300, 24576, "fp32", seed=93),
+    workloads.small("layernorm", 200, 22528, "bf16", "fp32", seed=94),
 ]
 
 
