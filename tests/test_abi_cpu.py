@@ -135,3 +135,23 @@ def test_binding_refuses_host_tensors(rn):
         rn.layernorm_bwd(x, x, w)
     with pytest.raises(ValueError, match="GPU tensor"):
         rn.fused_add_rmsnorm_fwd(x, x, w)
+
+
+def test_missing_library_raises(rn, tmp_path):
+    """No CPU fallback: loading from a path with no built library raises ImportError."""
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        rn.load_library(str(tmp_path / "librownorm.so"))
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package and its C sources name no oracle module: the oracle is test
+    infrastructure only."""
+    pkg = os.path.join(ROOT, "normalization_row_wise_amd")
+    offenders = []
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                if re.search(r"^\s*(import|from)\s+oracle\b|oracle/|\"oracle\"", src, re.M):
+                    offenders.append(f)
+    assert offenders == []
