@@ -227,11 +227,17 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
     if (block <= kLdsBudget) {
       s.acc = 1;
       R = o.rows ? o.rows : r_cap;
-      // RMSNorm with 256-thread teams and at least 16 rows per partial row: one team per
-      // workgroup.  Graph-replayed trainable steps, us: 8192 x 8192 bf16 131.0 -> 127.1,
-      // 8192 x 4096 fp32 128.7 -> 126.7, 4096 x 8192 bf16 72.2 -> 71.6; 2048 x 8192
-      // unchanged; LayerNorm (two gradients) and 192-thread teams were slower.
-      if (!o.rows && op == OP_RMS && s.team == 256 && M >= 16 * kMaxPartials) R = 1;
+      // RMSNorm over at least 8 rows per partial row, with teams of 64, 128 or 256
+      // threads that cover at least 2048 elements of a row: 256-thread workgroups.
+      // Graph-replayed trainable steps, us: 8192 x 8192 bf16 131.0 -> 127.1, 16384 x
+      // 4096 bf16 131.8 -> 129.6, 8192 x 4096 fp16 71.3 -> 69.9, 8192 x 2048 fp32 69.7
+      // -> 68.1, 8192 x 2048 bf16 41.5 -> 40.3, 2048 x 4096 bf16 28.1 -> 26.9; 2048 x
+      // 8192 unchanged.  Slower: 64-thread teams over 1024 elements (8192 x 1024 25.9 ->
+      // 26.2), 192-thread teams (8192 x 6144 100.7 -> 103.1) and LayerNorm (two
+      // gradients; 8192 x 4096 78.9 -> 83.4).
+      if (!o.rows && op == OP_RMS && M >= 8 * kMaxPartials && 256 % s.team == 0 &&
+          static_cast<int64_t>(s.team) * s.v >= 2048)
+        R = 256 / s.team;
       R = std::max(1, std::min(R, r_cap));
       s.shmem = block;
     } else if (s.v == 48 && ngrads == 2 && vec && s.team <= kAccS48 && block48 <= kLdsBudget) {
