@@ -234,8 +234,11 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
       // -> 68.1, 8192 x 2048 bf16 41.5 -> 40.3, 2048 x 4096 bf16 28.1 -> 26.9; 2048 x
       // 8192 unchanged.  Slower: 64-thread teams over 1024 elements (8192 x 1024 25.9 ->
       // 26.2), 192-thread teams (8192 x 6144 100.7 -> 103.1) and LayerNorm (two
-      // gradients; 8192 x 4096 78.9 -> 83.4).
-      if (!o.rows && op == OP_RMS && M >= 8 * kMaxPartials && 256 % s.team == 0 &&
+      // gradients; 8192 x 4096 78.9 -> 83.4).  The fused add gains from 32 rows per
+      // partial row on (Gemma bf16: 8192 x 4096 109.6 -> 106.6, 16384 x 4096 208.7 ->
+      // 204.5, 8192 x 2048 59.4 -> 58.7; 4096 x 4096 neutral).
+      const int64_t min_rows = op == OP_RMS ? 8 * kMaxPartials : 32 * kMaxPartials;
+      if (!o.rows && op != OP_LN && M >= min_rows && 256 % s.team == 0 &&
           static_cast<int64_t>(s.team) * s.v >= 2048)
         R = 256 / s.team;
       R = std::max(1, std::min(R, r_cap));

@@ -176,20 +176,25 @@ def test_wide_rows_one_row_ahead(wl):
     assert torch.equal(full["dx"].view(bits), frozen["dx"].view(bits))
 
 
-# RMSNorm over 2048 rows or more, with teams of 64, 128 or 256 threads that cover at
-# least 2048 elements: the trainable backward runs 256-thread workgroups of 4, 2 or 1
-# teams.  Row counts leave the last workgroups short; N is ragged where the team allows.
+# RMSNorm over 2048 rows or more (the fused add over 8192 or more), with teams of 64,
+# 128 or 256 threads that cover at least 2048 elements: the trainable backward runs
+# 256-thread workgroups of 4, 2 or 1 teams.  Row counts leave the last workgroups short; N is ragged where the team allows.
 RMS_TALL = [
     workloads.small("rmsnorm", 2100, 1500, "bf16", seed=101),    # teams of 64 (V = 32)
     workloads.small("rmsnorm", 2051, 4096, "bf16", seed=102),    # teams of 128
     workloads.small("rmsnorm", 2049, 2048, "fp32", seed=103),    # teams of 128 (V = 16)
     workloads.small("rmsnorm", 2300, 7000, "fp16", offset=1.0, weight="gemma", seed=104),
+    # the fused add from 8192 rows on: teams of 256 (one per workgroup; 33 or 32 rows per
+    # team, so the three-row prefetch ring ends at different points) and of 128 (two)
+    workloads.small("fused_add_rmsnorm", 8193, 4096, "bf16", offset=1.0, weight="gemma",
+                    seed=105),
+    workloads.small("fused_add_rmsnorm", 8200, 2000, "fp16", seed=106),
 ]
 
 
 @pytest.mark.parametrize("wl", RMS_TALL, ids=lambda c: c.name)
-def test_tall_rmsnorm_small_workgroups(wl):
-    _say("tall rmsnorm", wl.name)
+def test_tall_rows_small_workgroups(wl):
+    _say("tall rows", wl.name)
     fails = gp.check(wl, sample_rows=512)
     assert not fails, "\n".join(fails)
     t = workloads.generate(wl)
