@@ -1,22 +1,33 @@
 """Benchmark: row-wise norm forward + backward on one MI355X.
 
-One step = the whole path on one batch: forward (stats, normalise, affine) and
-backward (dx, per-workgroup dW/dB partials, column sum).  Default workload: LayerNorm
-2048 x 4096 bf16 with trainable weight and bias.  Prints ONE JSON line.
+One step = the whole path on one batch: forward (statistics, normalise, affine) and
+backward (dx and, for trainable parameters, the per-workgroup dW/dB partial rows, then
+the second kernel's fixed-order column sum).
+Default workload: RMSNorm 8192 x 8192 bf16 with a trainable weight, the largest of the
+named configurations.  Prints ONE JSON line.
 
-Timing.  Inputs are resident in HBM before the timed region.  S independent buffer
-sets (> 2x the 256 MiB MALL in total) rotate through the steps, and step k runs the
-forward on set k and the backward on set k + S/2, so every kernel reads data that the
-preceding steps have evicted from L2 and MALL: the numbers are HBM numbers.  The K
-timed steps are replayed from a HIP graph (captured once; the library's calls never
-allocate or synchronise), bracketed by synchronisation; ms_per_step = wall / K.  The
-dominant kernel (backward stage 1) is then timed live with HIP events on the launch
-stream over an eager pass of the same steps: an event before the backward call and
-the library's stage event between its two kernels.
+Timing protocol (after the Gemma page's "Benchmark results and measurement details":
+median of shuffled-provider rounds with an identical A/A duplicate as a control):
+  * Inputs are resident in HBM before any timed region.  S independent buffer sets
+    (more than three times the 256 MiB MALL in total) rotate through the steps: step k
+    runs the forward on set k and the backward on set k + S/2, so every kernel reads
+    data the preceding steps have evicted from L2 and MALL.
+  * Three providers, each a HIP graph of exactly --steps steps: "trainable", "frozen"
+    (dW/dB pruned: null outputs) and "trainable_aa", a second, identical capture of the
+    trainable step.  Each round replays every provider once, in a shuffled order, each
+    replay bracketed by synchronisation and timed with HIP events on its stream.
+  * Reported: the median over --rounds rounds of each provider's time per step; the
+    headline value is the trainable provider's; aa_delta_pct compares the two trainable
+    captures (run-to-run noise of the protocol itself).
+  * Per-kernel times (the roofline): an eager pass of the same steps queued behind a
+    spin kernel.  The forward kernel and the backward's first kernel (dx and the
+    partial rows) are launched with HIP events that the dispatch itself records (the
+    library's instrumentation hook, per thread); the whole backward call is bracketed
+    by ordinary HIP events on the launch stream.
 
-Algorithmic bytes (what the method must move, once each): forward reads x (and
+Algorithmic bytes (what the method must move, once each): forward reads x (and the
 residual), w (and b) and writes y (and residual_out) and the fp32 row statistics;
-backward reads dy, x (or residual_out), dres_out, w and writes dx and fp32 dW/dB.
+backward reads dy, x (or residual_out), dres_out, w and writes dx and the fp32 dW/dB.
 The backward recomputes the statistics from x, so it reads none.
 """
 from __future__ import annotations
@@ -24,6 +35,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import random
 import sys
 import time
 
@@ -84,14 +96,16 @@ def alg_bytes(wl: workloads.Workload, trainable: bool) -> dict:
 
 
 class Sets:
-    """S resident copies of one workload's inputs and outputs."""
+    """S resident copies of one workload's inputs and outputs, with the buffers of both
+    the trainable and the frozen backward (the frozen one passes null dW/dB)."""
 
-    def __init__(self, wl, S, trainable, rn, torch):
+    def __init__(self, wl, S, rn, torch):
         self.wl, self.S, self.rn, self.torch = wl, S, rn, torch
         base = workloads.generate(wl)
         dev = torch.device("cuda:0")
         self.eps, self.off = base["eps"], base["offset"]
         M, N = wl.M, wl.N
+        ngr = 2 if wl.op == "layernorm" else 1
         self.sets = []
         for s in range(S):
             d = {}
@@ -108,12 +122,11 @@ class Sets:
                 d["mean"] = torch.empty(M, dtype=torch.float32, device=dev)
             if wl.op == "fused_add_rmsnorm":
                 d["ro"] = torch.empty_like(d["x"])
-            ngr = (2 if wl.op == "layernorm" else 1) if trainable else 0
-            d["dw"] = torch.empty(N, dtype=torch.float32, device=dev) if trainable else None
-            d["db"] = (torch.empty(N, dtype=torch.float32, device=dev)
-                       if trainable and wl.op == "layernorm" else None)
-            need = rn.workspace_bytes(M, N, ngr) if ngr else 0
-            d["ws"] = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+            d["dw"] = torch.empty(N, dtype=torch.float32, device=dev)
+            d["db"] = torch.empty(N, dtype=torch.float32, device=dev) if wl.op == "layernorm" \
+                else None
+            # zero-filled once: the library's hand-over counters live at its start
+            d["ws"] = rn.new_workspace(rn.workspace_bytes(M, N, ngr), dev)
             self.sets.append(d)
         self.bytes_per_set = sum(v.numel() * v.element_size() for v in self.sets[0].values()
                                  if isinstance(v, torch.Tensor))
@@ -129,21 +142,23 @@ class Sets:
             rn.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["w"], self.eps, self.off, y=d["y"],
                                      residual_out=d["ro"], rstd=d["rstd"])
 
-    def bwd(self, s):
+    def bwd(self, s, trainable):
         d, rn, wl = self.sets[s], self.rn, self.wl
+        dw = d["dw"] if trainable else None
+        ws = d["ws"] if trainable else None
         if wl.op == "rmsnorm":
-            rn.rmsnorm_bwd(d["dy"], d["x"], d["w"], self.eps, self.off, dx=d["dx"], dw=d["dw"],
-                           workspace=d["ws"])
+            rn.rmsnorm_bwd(d["dy"], d["x"], d["w"], self.eps, self.off, dx=d["dx"], dw=dw,
+                           workspace=ws)
         elif wl.op == "layernorm":
-            rn.layernorm_bwd(d["dy"], d["x"], d["w"], self.eps, dx=d["dx"], dw=d["dw"], db=d["db"],
-                             workspace=d["ws"])
+            rn.layernorm_bwd(d["dy"], d["x"], d["w"], self.eps, dx=d["dx"], dw=dw,
+                             db=d["db"] if trainable else None, workspace=ws)
         else:
             rn.fused_add_rmsnorm_bwd(d["dy"], d["ro"], d["w"], self.eps, self.off, d.get("dres"),
-                                     dx=d["dx"], dw=d["dw"], workspace=d["ws"])
+                                     dx=d["dx"], dw=dw, workspace=ws)
 
-    def step(self, k):
+    def step(self, k, trainable):
         self.fwd(k % self.S)
-        self.bwd((k + self.S // 2) % self.S)
+        self.bwd((k + self.S // 2) % self.S, trainable)
 
 
 MAX_SETS = 256
@@ -159,46 +174,72 @@ def n_sets(bytes_per_set: int) -> int:
     return max(s, 4)
 
 
-def time_steps(sets, K, W, use_graph, torch):
-    """Wall-clock seconds for K steps (after W warmup steps)."""
+PROVIDERS = ("trainable", "frozen", "trainable_aa")
+
+
+def capture(sets, K, trainable, torch):
+    """A HIP graph of exactly K steps (the library's calls never allocate or
+    synchronise, so they capture as they are)."""
+    g = torch.cuda.CUDAGraph()
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for k in range(K):
+                sets.step(k, trainable)
+    torch.cuda.synchronize()
+    return g
+
+
+def median(a):
+    a = sorted(a)
+    n = len(a)
+    return a[n // 2] if n % 2 else 0.5 * (a[n // 2 - 1] + a[n // 2])
+
+
+def time_rounds(sets, K, W, rounds, torch, seed=0):
+    """Per-step device time (us) of each provider: median over `rounds` rounds of one
+    replay of each provider's K-step graph, providers in a shuffled order per round.
+    Returns ({provider: median us/step}, {provider: [us/step per round]}, wall seconds
+    of the timed replays)."""
     for k in range(W):
-        sets.step(k)
+        sets.step(k, True)
+        sets.step(k, False)
     torch.cuda.synchronize()
-    if use_graph:
-        # one graph holds a whole number of passes over the sets, at least 64 steps
-        G = sets.S * max(1, -(-64 // sets.S))
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for k in range(G):
-                    sets.step(k)
-        torch.cuda.synchronize()
-        reps = max(1, K // G)
-        g.replay()  # one untimed replay
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, reps * G
-    t0 = time.perf_counter()
-    for k in range(K):
-        sets.step(k)
+    graphs = {p: capture(sets, K, p != "frozen", torch) for p in PROVIDERS}
+    for g in graphs.values():   # one untimed replay each
+        g.replay()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0, K
+    st = torch.cuda.current_stream()
+    rng = random.Random(seed)
+    per = {p: [] for p in PROVIDERS}
+    wall = 0.0
+    for _ in range(rounds):
+        order = list(PROVIDERS)
+        rng.shuffle(order)
+        for p in order:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record(st)
+            graphs[p].replay()
+            e1.record(st)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+            per[p].append(e0.elapsed_time(e1) * 1e3 / K)
+    del graphs
+    return {p: median(v) for p, v in per.items()}, per, wall
 
 
-def event_times(sets, n, rn, torch):
-    """Per-kernel device times (us) from HIP events on the launch stream.
-
-    The forward kernel and the first backward kernel (dx + partial rows) are launched
-    through hipExtLaunchKernel with a start/stop event pair, so each pair brackets
-    exactly one kernel (the dispatch records both).  The whole backward call (both
-    kernels) is bracketed by ordinary events.  A spin kernel holds the GPU while the
-    host enqueues every step, so the GPU then runs them back to back."""
+def call_times(sets, n, trainable, torch):
+    """Per-kernel and per-call device times (us): an eager pass of n steps queued behind
+    a spin kernel (so the GPU runs them back to back).  The forward kernel and the
+    backward's first kernel record dispatch events (instrumentation hook); the whole
+    backward call (with parameter gradients: two kernels) is bracketed by HIP events on
+    the launch stream."""
+    rn = sets.rn
     st = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)
     ev = [[mk() for _ in range(6)] for _ in range(n)]
@@ -206,32 +247,35 @@ def event_times(sets, n, rn, torch):
         e.record(st)                      # materialise the event handles
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * (0.002 + 40e-6 * n)))   # ~ 2 ms + 40 us per step
-    for k in range(n):
-        f0, f1, b0, b1, c0, c1 = ev[k]
-        rn.set_timing_events(0, f0, f1)
-        sets.fwd(k % sets.S)
-        rn.set_timing_events(0, None, None)
-        rn.set_timing_events(1, b0, b1)
-        c0.record(st)
-        sets.bwd((k + sets.S // 2) % sets.S)
-        c1.record(st)
-        rn.set_timing_events(1, None, None)
+    try:
+        for k in range(n):
+            f0, f1, k0, k1, b0, b1 = ev[k]
+            rn._set_timing_events(0, f0, f1)
+            sets.fwd(k % sets.S)
+            rn._set_timing_events(0, None, None)
+            rn._set_timing_events(1, k0, k1)
+            b0.record(st)
+            sets.bwd((k + sets.S // 2) % sets.S, trainable)
+            b1.record(st)
+            rn._set_timing_events(1, None, None)
+    finally:
+        rn._set_timing_events(0, None, None)
+        rn._set_timing_events(1, None, None)
     torch.cuda.synchronize()
     f = [ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(n)]
-    b1 = [ev[k][2].elapsed_time(ev[k][3]) * 1e3 for k in range(n)]
+    k1 = [ev[k][2].elapsed_time(ev[k][3]) * 1e3 for k in range(n)]
     b = [ev[k][4].elapsed_time(ev[k][5]) * 1e3 for k in range(n)]
-    med = lambda a: sorted(a)[len(a) // 2]
-    mean = lambda a: sum(a) / len(a)
-    return {"fwd_us_median": med(f), "bwd_stage1_us_median": med(b1), "bwd_us_median": med(b),
-            "bwd_stage1_us_mean": mean(b1), "fwd_us_mean": mean(f)}
+    return {"fwd_us_median": median(f), "fwd_us_mean": sum(f) / n,
+            "bwd_kernel1_us_median": median(k1), "bwd_kernel1_us_mean": sum(k1) / n,
+            "bwd_us_median": median(b), "bwd_us_mean": sum(b) / n}
 
 
 def stream_ceiling(sets, n, torch) -> dict:
-    """Context for the stage-1 roofline: torch's own elementwise kernel moving the same
-    row tensors as the backward's first kernel (2 reads + 1 write; the fused add's 3 + 1),
-    on the same rotating buffer sets, timed like the library's kernels (events around
-    each launch, queued behind a spin kernel).  No reduction, no fp64: what streaming
-    alone reaches on this GPU for this size."""
+    """Context for the backward roofline: torch's own elementwise kernel moving the same
+    row tensors as the backward (2 reads + 1 write; the fused add's 3 + 1), on the same
+    rotating buffer sets, timed like the library's calls (events around each launch,
+    queued behind a spin kernel).  No reduction, no fp64: what streaming alone reaches
+    on this GPU for this size."""
     fused = sets.wl.op == "fused_add_rmsnorm"
     st = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)
@@ -255,24 +299,30 @@ def stream_ceiling(sets, n, torch) -> dict:
         op(k)
         ev[k][1].record(st)
     torch.cuda.synchronize()
-    t = sorted(ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(n))[n // 2]
+    t = median([ev[k][0].elapsed_time(ev[k][1]) * 1e3 for k in range(n)])
     x = sets.sets[0]["x"]
     nbytes = x.numel() * x.element_size() * (4 if fused else 3)
     return {"op": "torch.addcmul, 3 reads + 1 write" if fused else "torch.mul, 2 reads + 1 write",
             "us_median": round(t, 3), "gbs": round(nbytes / (t * 1e-6) / 1e9, 1)}
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
-    """The oracle (numpy fp64, as it stands) on a bounded sample of the workload's rows,
-    forward + backward: first on one thread, repeated until `budget_s` has passed, then
-    on every host core the process may use (at most 16): one thread per core, each
-    running the same oracle calls on the sample, in rounds until `budget_s` has passed
-    again.  numpy releases the interpreter lock inside its array loops, so the threads
-    run in parallel.  Each figure is the median over the repetitions (rounds)."""
+# Threads the CPU baseline may use: one GPU's share of the host's cores on the GPU
+# machines (16), or fewer when the process may use fewer.
+CPU_SHARE = 16
+
+
+def cpu_baseline(wl, budget_s: float, rows: int = 256) -> dict:
+    """The oracle (numpy fp64, as it stands, never tuned) on a bounded sample of the
+    workload's rows, forward + backward, on the host: every usable core (at most one
+    GPU's share, CPU_SHARE threads), each thread running the same oracle calls on the
+    sample, in rounds until `budget_s` has passed; then on one thread for another
+    `budget_s`.  numpy releases the interpreter lock inside its array loops, so the
+    threads run in parallel.  Each figure is the median round (repetition), as the
+    sample's algorithmic bytes per second."""
     from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
-    rows = min(wl.M, 256)
+    rows = min(wl.M, rows)
     t = workloads.generate(wl, rows=slice(0, rows))
     f = workloads.as_f64
     x, dy, w = f(t["x"]), f(t["dy"]), f(t["w"])
@@ -304,20 +354,21 @@ def cpu_baseline(wl, budget_s: float) -> dict:
             times.append(time.perf_counter() - a)
         return float(np.median(times)), len(times), time.perf_counter() - t0
 
-    per, n, el = timed(step)
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    usable = len(os.sched_getaffinity(0))
+    cores = max(1, min(usable, CPU_SHARE))
     with ThreadPoolExecutor(max_workers=cores) as pool:
         list(pool.map(step, range(cores)))  # start the threads before timing
         per_all, n_all, el_all = timed(lambda: list(pool.map(step, range(cores))))
-    return {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+    per, n, el = timed(step)
+    return {"value": round(cores * step_bytes / per_all / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{rows} of {wl.M} rows x {wl.N}, fwd+bwd, median of {n} repetitions "
-                      f"in {el:.1f} s (numpy fp64, single thread)",
-            "us_per_step_of_sample": round(per * 1e6, 1),
-            "all_cores": {"value": round(cores * step_bytes / per_all / 1e9, 4), "unit": "GB/s",
-                          "cores": cores,
-                          "sample": f"{cores} threads, each the same {rows}-row fwd+bwd; median "
-                                    f"of {n_all} rounds in {el_all:.1f} s"},
+            "sample": f"{rows} of {wl.M} rows x {wl.N}, fwd+bwd (numpy fp64); {cores} threads "
+                      f"each running it, median of {n_all} rounds in {el_all:.1f} s",
+            "usable_cpus": usable,
+            "thread_cap": f"at most {CPU_SHARE} threads (one GPU's share of the host)",
+            "single_thread": {"value": round(step_bytes / per / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "us_per_step_of_sample": round(per * 1e6, 1),
+                              "sample": f"median of {n} repetitions in {el:.1f} s"},
             "cpu_model": _cpu_model()}
 
 
@@ -331,18 +382,50 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+# Configurations timed beside the headline, reported as extra keys of the same line.
+EXTRA = ("layernorm_2048x4096_bf16", "fused_add_rmsnorm_2048x8192_bf16")
+
+
+def measure(wl, K, W, rounds, rn, torch, event_steps):
+    """The protocol above on one workload: providers' median step times, A/A delta,
+    per-call kernel times and the step's algorithmic GB/s."""
+    probe = Sets(wl, 1, rn, torch)
+    S = n_sets(probe.bytes_per_set)
+    cold = S * probe.bytes_per_set >= 3 * MALL_BYTES
+    del probe
+    sets = Sets(wl, S, rn, torch)
+    med, per, wall = time_rounds(sets, K, W, rounds, torch)
+    ev_t = call_times(sets, event_steps, True, torch)
+    ev_f = call_times(sets, event_steps, False, torch)
+    abt, abf = alg_bytes(wl, True), alg_bytes(wl, False)
+    out = {
+        "sets": sets, "S": S, "cold": cold, "wall": wall, "per_round": per,
+        "us_per_step": {p: round(med[p], 3) for p in PROVIDERS},
+        "aa_delta_pct": round(100 * (med["trainable_aa"] / med["trainable"] - 1), 2),
+        "gbs": abt["step"] / (med["trainable"] * 1e-6) / 1e9,
+        "frozen_gbs": abf["step"] / (med["frozen"] * 1e-6) / 1e9,
+        "calls": {"fwd_kernel_us": round(ev_t["fwd_us_median"], 3),
+                  "bwd_trainable_kernel1_us": round(ev_t["bwd_kernel1_us_median"], 3),
+                  "bwd_trainable_call_us": round(ev_t["bwd_us_median"], 3),
+                  "bwd_frozen_kernel_us": round(ev_f["bwd_kernel1_us_median"], 3),
+                  "bwd_frozen_call_us": round(ev_f["bwd_us_median"], 3)},
+        "ev_t": ev_t, "ev_f": ev_f,
+    }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default=workloads.LAYERNORM_2048x4096.name,
+    ap.add_argument("--steps", type=int, default=20, help="steps per timed replay")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rounds", type=int, default=9)
+    ap.add_argument("--config", default=workloads.RMS_8192x8192.name,
                     choices=sorted(workloads.BY_NAME))
-    ap.add_argument("--frozen", action="store_true", help="time the frozen-parameter step")
-    ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    ap.add_argument("--no-extra", action="store_true", help="skip the extra configurations")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--event-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
+    ap.add_argument("--event-steps", type=int, default=100)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -363,6 +446,9 @@ def main():
               "would shard across GPUs with no communication except one all-reduce of "
               "dW/dB).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.rounds < 1:
+        print("--steps and --rounds must be at least 1", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import __graft_entry__
@@ -370,67 +456,68 @@ def main():
     import normalization_row_wise_amd as rn
 
     wl = workloads.BY_NAME[args.config]
-    trainable = not args.frozen
-    probe = Sets(wl, 1, trainable, rn, torch)
-    S = n_sets(probe.bytes_per_set)
-    cold = S * probe.bytes_per_set >= 3 * MALL_BYTES
-    del probe
-    sets = Sets(wl, S, trainable, rn, torch)
-
-    secs, k = time_steps(sets, args.steps, args.warmup, not args.eager, torch)
-    ab = alg_bytes(wl, trainable)
-    ms = secs / k * 1e3
-    gbs = ab["step"] * k / secs / 1e9
-    ev = event_times(sets, args.event_steps, rn, torch)
-
-    # frozen-parameter variant of the same step (context for the pruning)
-    other = {}
-    if trainable:
-        fz = Sets(wl, S, False, rn, torch)
-        fsecs, fk = time_steps(fz, args.steps, args.warmup, not args.eager, torch)
-        fev = event_times(fz, args.event_steps, rn, torch)
-        other = {"frozen_us_per_step": round(fsecs / fk * 1e6, 3),
-                 "frozen_bwd_kernel_us": round(fev["bwd_stage1_us_median"], 3)}
-        del fz
-
+    m = measure(wl, args.steps, args.warmup, args.rounds, rn, torch, args.event_steps)
+    sets = m["sets"]
+    abt = alg_bytes(wl, True)
     ceiling = stream_ceiling(sets, args.event_steps, torch) if "dres" in sets.sets[0] or \
-        sets.wl.op != "fused_add_rmsnorm" else None
-    stage1_us = ev["bwd_stage1_us_mean"]
-    achieved = ab["bwd_stage1"] / (stage1_us * 1e-6) / 1e9
-    kernel_key = "bwd_stage1_trainable" if trainable else "bwd_frozen"
-    traffic = measured_traffic(wl.name, kernel_key)
+        wl.op != "fused_add_rmsnorm" else None
+    # dominant kernel: the trainable backward's first kernel (dx, partial rows of dW)
+    k1_us = m["ev_t"]["bwd_kernel1_us_mean"]
+    achieved = abt["bwd_stage1"] / (k1_us * 1e-6) / 1e9
+    traffic = measured_traffic(wl.name, "bwd_stage1_trainable")
+    del m["sets"], sets
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        for name in EXTRA:
+            if name == wl.name:
+                continue
+            e = measure(workloads.BY_NAME[name], args.steps, args.warmup, args.rounds, rn, torch,
+                        args.event_steps)
+            extra[name] = {
+                "us_per_step": e["us_per_step"], "aa_delta_pct": e["aa_delta_pct"],
+                "gbs": round(e["gbs"], 1), "pct_of_hbm_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 2),
+                "frozen_gbs": round(e["frozen_gbs"], 1), "us_per_call": e["calls"]}
+            del e["sets"], e
+            torch.cuda.empty_cache()
+
+    med = m["us_per_step"]
     line = {
         "metric": "achieved HBM GB/s (% of peak) & µs/call, bf16 norm fwd+bwd at M×N",
-        "value": round(gbs, 2),
+        "value": round(m["gbs"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": k,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(med["trainable"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        # arithmetic type: row statistics, LayerNorm outputs and dx are formed in fp64
-        # (storage type of the activations: config.io)
-        "dtype": "f64",
+        # arithmetic: row sums, dx and LayerNorm y in fp64; RMSNorm y and the dW/dB
+        # accumulation in fp32; storage (config.io) bf16
+        "dtype": "f64+f32",
+        "arithmetic": {"row_sums": "f64", "dx": "f64", "y": "f32 (RMSNorm), f64 (LayerNorm)",
+                       "dW_dB": "f32", "storage": wl.io},
         "data": "synthetic (seeded CPU randn, no dataset)",
         "config": {"workload": wl.name, "op": wl.op, "M": wl.M, "N": wl.N, "io": wl.io,
-                   "weight": wl.wt, "trainable_params": trainable,
-                   "timing": "eager" if args.eager else "hip graph replay", "buffer_sets": S,
-                   "inputs_cold_in_mall": cold},
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "us_per_call": {"fwd_kernel": round(ev["fwd_us_median"], 3),
-                        "bwd_stage1_kernel": round(ev["bwd_stage1_us_median"], 3),
-                        "bwd_call_events": round(ev["bwd_us_median"], 3),
-                        "step_wall": round(ms * 1e3, 3)},
-        **other,
-        "roofline": {"kernel": "bwd_kernel (stage 1: dx + dW/dB partial rows)" if trainable
-                     else "bwd_kernel (frozen parameters: dx only)",
+                   "weight": wl.wt, "trainable_params": True,
+                   "timing": f"median of {args.rounds} shuffled rounds of HIP-graph replays of "
+                             f"{args.steps} steps (providers trainable, frozen, trainable A/A)",
+                   "buffer_sets": m["S"], "inputs_cold_in_mall": m["cold"]},
+        "pct_of_hbm_peak": round(100 * m["gbs"] / HBM_PEAK_GBS, 2),
+        "us_per_step": med,
+        "aa_delta_pct": m["aa_delta_pct"],
+        "frozen_gbs": round(m["frozen_gbs"], 1),
+        "us_per_call": m["calls"],
+        "timed_replays_wall_s": round(m["wall"], 4),
+        "roofline": {"kernel": "bwd_kernel (stage 1: dx + dW partial rows)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "alg_bytes_per_launch": ab["bwd_stage1"],
-                     "avg_launch_us": round(stage1_us, 3),
+                     "alg_bytes_per_launch": abt["bwd_stage1"],
+                     "avg_launch_us": round(k1_us, 3),
                      "stream_ceiling": ceiling},
+        "extra_configs": extra,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

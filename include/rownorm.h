@@ -40,7 +40,14 @@
  *     16-bit output is at most 1 unit in the last place from the correctly rounded
  *     value).  RMSNorm y is formed in fp32 from (float)w + offset.
  *   - Errors: arguments are checked before any HIP call; on error nothing is enqueued
- *     and an rn_status < 0 is returned.  RN_ERR_HIP reports a failed launch.
+ *     and an rn_status < 0 is returned.  RN_ERR_HIP reports that the HIP runtime refused
+ *     one of this call's launches (the status of that launch itself, not an error left
+ *     behind by earlier HIP work).  The library keeps no mutable process-wide state.
+ *   - Backward workspace (parameter gradients only): caller-owned device memory of at
+ *     least rn_bwd_workspace_bytes() bytes, 16-byte aligned, any contents; it holds the
+ *     per-workgroup partial rows of dw / db between the two kernels of one call.  One
+ *     workspace must not be used by two calls that can run at the same time (different
+ *     streams without ordering).
  *   - Aliasing: an output may alias an input of the same shape and stride (y == x,
  *     residual_out == residual, dx == dy or dx == dres_out): such calls run kernels
  *     in which each element is read before it is written by the same thread (never
@@ -72,19 +79,20 @@ typedef enum rn_status {
   RN_ERR_STRIDE = -4,     /* a row stride below N                                  */
   RN_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than rn_bwd_workspace_bytes */
   RN_ERR_HIP = -6,        /* a kernel launch failed                                */
-  RN_ERR_ALIAS = -7       /* two outputs share storage                             */
+  RN_ERR_ALIAS = -7,      /* two outputs share storage                             */
+  RN_ERR_INTERNAL = -8    /* no compiled kernel instance for the planned launch    */
 } rn_status;
 
 #define RN_MAX_N 24576
 
 /* Bytes of workspace a backward call needs for `n_param_grads` (0, 1 or 2) fp32
- * parameter gradients at this shape: per-workgroup partial rows of dw / db,
- * reduced by a second kernel in fixed order.  0 when n_param_grads == 0 (frozen
- * parameters need no workspace: [frozen], Motivation).  Returns 0 for invalid shapes.
- * When the call has a single partial row (very small M: one workgroup covering every
- * row, or one row spread over workgroups) and dw / db are 16-byte aligned, the
- * gradients are written directly and the workspace is left untouched; it must still
- * be passed. */
+ * parameter gradients at this shape ([frozen], Motivation: per-program partial rows of
+ * dw / db written by the first kernel, then summed over the rows by a second kernel, in
+ * a fixed order).  0 when n_param_grads == 0 (frozen parameters need no workspace and
+ * get no second kernel).  Returns 0 for invalid shapes.  When the call has a single
+ * partial row (very small M: one workgroup covering every row, or one row spread over
+ * workgroups) and dw / db are 16-byte aligned, the gradients are written directly and
+ * the workspace is left untouched; it must still be passed. */
 size_t rn_bwd_workspace_bytes(int64_t M, int64_t N, int n_param_grads);
 
 /* RMSNorm forward.  [gemma] Summary: offset added to the weight in fp32 in-kernel.
@@ -100,7 +108,12 @@ int rmsnorm_fwd(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy,
  *   dx [M, lddx] out (may equal dy), dw [N] fp32 out or NULL (frozen weight: no
  *   workspace, no partials, no second kernel), ws / ws_bytes: workspace of at least
  *   rn_bwd_workspace_bytes(M, N, dw != NULL) bytes (may be NULL / 0 when dw is NULL).
- *   The row statistics are recomputed from x in fp64 (no saved rstd is taken). */
+ *   Statistics: this entry point takes eps where a plain rendering of the method would
+ *   take the forward's saved rstd.  It recomputes the row's statistics from x in fp64
+ *   while it reads x anyway (no extra HBM traffic): a saved fp32 rstd carries a 2^-24
+ *   relative error that the cancellation in g - xhat * mean(g * xhat) turns into
+ *   whole-unit errors of small 16-bit dx values.  The forward's rstd output is
+ *   therefore informational (it may be NULL). */
 int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
                 void* dx, int64_t lddx, float* dw, void* ws, size_t ws_bytes,
                 int64_t M, int64_t N, float eps, float offset,
@@ -115,7 +128,10 @@ int layernorm_fwd(const void* x, int64_t ldx, const void* w, const void* b, void
 
 /* LayerNorm backward.  [frozen] Key Changes: dW and dB are pruned independently.
  *   dw, db: fp32 [N] out, each may be NULL.  Workspace of at least
- *   rn_bwd_workspace_bytes(M, N, (dw != NULL) + (db != NULL)) bytes. */
+ *   rn_bwd_workspace_bytes(M, N, (dw != NULL) + (db != NULL)) bytes.
+ *   Statistics: takes eps instead of the forward's saved mean / rstd and recomputes
+ *   them from x in fp64, for the reason given at rmsnorm_bwd; the forward's mean and
+ *   rstd outputs are informational (they may be NULL). */
 int layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
                   void* dx, int64_t lddx, float* dw, float* db, void* ws, size_t ws_bytes,
                   int64_t M, int64_t N, float eps, rn_dtype xt, rn_dtype wt,
@@ -134,7 +150,9 @@ int fused_add_rmsnorm_fwd(const void* x, int64_t ldx, const void* residual, int6
  * gradient; the backward works from the rounded saved residual).
  *   dy in; dres_out in or NULL (no gradient reaches residual_out); residual_out in
  *   (the forward's output); dx out = gradient of x and of residual (may equal dy or
- *   dres_out); dw fp32 out or NULL; workspace as for rmsnorm_bwd. */
+ *   dres_out); dw fp32 out or NULL; workspace as for rmsnorm_bwd.
+ *   Statistics: takes eps instead of the forward's saved rstd and recomputes it from
+ *   residual_out in fp64, for the reason given at rmsnorm_bwd. */
 int fused_add_rmsnorm_bwd(const void* dy, int64_t lddy, const void* dres_out, int64_t lddr,
                           const void* residual_out, int64_t ldro, const void* w, void* dx,
                           int64_t lddx, float* dw, void* ws, size_t ws_bytes, int64_t M,
@@ -143,22 +161,6 @@ int fused_add_rmsnorm_bwd(const void* dy, int64_t lddy, const void* dres_out, in
 
 /* Human-readable name of a status code (static storage). */
 const char* rn_status_str(int status);
-
-/* Launch-shape override for tuning sweeps (0 = automatic for every field).
- *   kind 0 = forward kernels, 1 = backward kernels with parameter gradients,
- *   2 = backward kernels without them.  v: elements per thread per row (one of the
- *   compiled sizes), rows: rows per workgroup pass, wg_rows: rows per workgroup in
- *   total (backward partial-row granularity).  Process-wide; not thread-safe; a
- *   shape that cannot run the problem is ignored.  Returns RN_OK or RN_ERR_SHAPE. */
-int rn_set_launch_override(int kind, int v, int rows, int wg_rows);
-
-/* Instrumentation for timing single kernels.  While `start` and `stop` are not NULL,
- * every launch of the chosen kernel family records its own start and end times into
- * them (hipExtLaunchKernel events, taken by the dispatch itself): kernel 0 = forward
- * kernels, 1 = first backward kernel (dx and partial rows).  Pass NULLs to stop.
- * Process-wide; not thread-safe.  Returns RN_OK, or RN_ERR_SHAPE for another
- * kernel number. */
-int rn_set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

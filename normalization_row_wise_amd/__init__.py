@@ -26,8 +26,6 @@ _vp, _i64, _f32, _i32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, c
 _SIGS = {
     "rn_bwd_workspace_bytes": (_sz, [_i64, _i64, _i32]),
     "rn_status_str": (ctypes.c_char_p, [_i32]),
-    "rn_set_launch_override": (_i32, [_i32, _i32, _i32, _i32]),
-    "rn_set_timing_events": (_i32, [_i32, _vp, _vp]),
     "rmsnorm_fwd": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _f32, _f32, _i32, _i32, _vp]),
     "rmsnorm_bwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _i64, _i64, _f32,
                            _f32, _i32, _i32, _vp]),
@@ -42,6 +40,10 @@ _SIGS = {
 }
 
 
+# Instrumentation (normalization_row_wise_amd/csrc/rn_instrument.h; not the product ABI).
+_INSTRUMENT_SIGS = {"rn_set_timing_events": (_i32, [_i32, _vp, _vp])}
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load the HIP library and declare its C signatures.  Raises if it is missing."""
     if not os.path.exists(path):
@@ -53,6 +55,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
+    for name, (res, args) in _INSTRUMENT_SIGS.items():   # optional
+        f = getattr(lib, name, None)
+        if f is not None:
+            f.restype = res
+            f.argtypes = args
     return lib
 
 
@@ -120,18 +127,21 @@ def _workspace(ws, M, N, n, device):
         need = workspace_bytes(M, N, n) if n else 0
         if need == 0:
             return None, 0
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = new_workspace(need, device)
     return ws, ws.numel() * ws.element_size()
 
 
-def set_launch_override(kind: int, v: int = 0, rows: int = 0, wg_rows: int = 0) -> None:
-    _check(lib.rn_set_launch_override(kind, v, rows, wg_rows))
+def new_workspace(nbytes: int, device=None):
+    """A backward workspace of nbytes (device memory for the per-workgroup partial rows
+    of dW / dB; its contents do not matter)."""
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def set_timing_events(kernel: int, start=None, stop=None) -> None:
-    """Time every launch of one kernel family with two torch.cuda.Events (recorded by
-    the dispatch itself): kernel 0 = forward, 1 = first backward kernel.  The events
-    must have been recorded once (so that they exist).  None, None stops."""
+def _set_timing_events(kernel: int, start=None, stop=None) -> None:
+    """Instrumentation for measurement harnesses: every launch of one kernel family made
+    by this thread records its dispatch start / end into two torch.cuda.Events (kernel 0
+    = forward, 1 = the backward's first kernel).  The events must have been recorded
+    once (so that they exist).  None, None stops."""
     h = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
     _check(lib.rn_set_timing_events(kernel, h(start), h(stop)))
 
@@ -223,8 +233,7 @@ def fused_add_rmsnorm_bwd(dy, residual_out, w, eps: float = 1e-6, offset: float 
 
 
 __all__ = [
-    "lib", "LIB_PATH", "RowNormError", "workspace_bytes", "set_launch_override",
-    "set_timing_events",
+    "lib", "LIB_PATH", "RowNormError", "workspace_bytes", "new_workspace",
     "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
     "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_bwd",
 ]

@@ -6,6 +6,7 @@
 #include <cstdint>
 
 #include "../../include/rownorm.h"
+#include "rn_instrument.h"
 #include "rn_launch.h"
 
 namespace rn {
@@ -92,12 +93,6 @@ inline int64_t max_partials(int64_t N) { return N <= kNarrowN ? kMaxPartialsNarr
 #endif
 constexpr size_t kLdsBudget = RN_LDS_BUDGET;
 
-struct Override {
-  int v = 0, rows = 0, wg_rows = 0;
-};
-Override g_override[3];  // 0: forward, 1: backward with grads, 2: backward without
-hipEvent_t g_timing[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};  // [kernel][start, stop]
-
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 inline int64_t ldws_of(int64_t N) { return round_up(N, 64); }
@@ -141,8 +136,7 @@ inline int64_t team_of(int64_t N, int v) { return round_up(cdiv(N, v), 64); }
 
 inline int max_wg(int kind, int v, int eb) { return kind == 0 ? fwd_max_wg(v, eb) : bwd_max_wg(v, eb); }
 
-inline int pick_v(int kind, int op, int64_t N, int eb, int requested) {
-  if (requested && team_of(N, requested) <= max_wg(kind, requested, eb)) return requested;
+inline int pick_v(int kind, int op, int64_t N, int eb) {
   const int pref = eb == 2 ? (op == OP_FADD ? 16 : 32) : 16;
   for (int v : kVs) {
     if (v > pref) break;
@@ -188,9 +182,8 @@ inline int narrow_team(int64_t N, bool vec, int64_t max_ld, int eb) {
 // max_ld: the widest row stride of the call's row tensors.
 Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec, int64_t max_ld) {
   Shape s;
-  const Override& o = g_override[kind];
   const int eb = elem_bytes(xt);
-  if (const int ts = o.v ? 0 : narrow_team(N, vec, max_ld, eb)) {
+  if (const int ts = narrow_team(N, vec, max_ld, eb)) {
     s.v = 8;
     s.team = ts;
     s.ts = ts;
@@ -207,14 +200,13 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
     } else {
       rows = round_up(cdiv(M, kTargetGrid), R);
     }
-    if (o.wg_rows && kind != 1) rows = round_up(o.wg_rows, R);
     rows = std::max<int64_t>(rows, round_up(cdiv(M, int64_t(1) << 30), R));
     s.rows_per_wg = rows;
     s.grid = M > 0 ? cdiv(M, rows) : 0;
     s.P = kind == 1 ? static_cast<int>(s.grid) : 0;
     return s;
   }
-  s.v = pick_v(kind, op, N, eb, o.v);
+  s.v = pick_v(kind, op, N, eb);
   s.team = static_cast<int>(team_of(N, s.v));
   const int wg_cap = max_wg(kind, s.v, eb);
   const int r_cap = wg_cap / s.team;
@@ -226,7 +218,7 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
     const size_t block48 = static_cast<size_t>(ngrads) * s.v * kAccS48 * sizeof(float);
     if (block <= kLdsBudget) {
       s.acc = 1;
-      R = o.rows ? o.rows : r_cap;
+      R = r_cap;
       // RMSNorm over at least 8 rows per partial row, with teams of 64, 128 or 256
       // threads that cover at least 2048 elements of a row: 256-thread workgroups.
       // Graph-replayed trainable steps, us: 8192 x 8192 bf16 131.0 -> 127.1, 16384 x
@@ -238,11 +230,21 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
       // partial row on (Gemma bf16: 8192 x 4096 109.6 -> 106.6, 16384 x 4096 208.7 ->
       // 204.5, 8192 x 2048 59.4 -> 58.7; 4096 x 4096 neutral).
       const int64_t min_rows = op == OP_RMS ? 8 * kMaxPartials : 32 * kMaxPartials;
-      if (!o.rows && op != OP_LN && M >= min_rows && 256 % s.team == 0 &&
+      if (op != OP_LN && M >= min_rows && 256 % s.team == 0 &&
           static_cast<int64_t>(s.team) * s.v >= 2048)
         R = 256 / s.team;
       R = std::max(1, std::min(R, r_cap));
       s.shmem = block;
+      // RMSNorm with one 256-thread team per workgroup: dW accumulates in registers (one
+      // workgroup per CU leaves the VGPRs: 162 at V = 32) instead of a read-modify-write
+      // of its LDS block per row.  Trainable 8192 x 8192 bf16 backward (both kernels,
+      // events around the call) 91.6 -> 88.5 us.  Slower with several teams to combine
+      // (LayerNorm 2048 x 4096 23.9 -> 36.1 us) and for the fused add's three-row ring
+      // (2048 x 8192 37.6 -> 39.9 us), so only here.
+      if (op == OP_RMS && R == 1 && s.team == 256 && (s.v == 16 || s.v == 32)) {
+        s.acc = 0;
+        s.shmem = 0;
+      }
     } else if (s.v == 48 && ngrads == 2 && vec && s.team <= kAccS48 && block48 <= kLdsBudget) {
       s.acc = 2;
       R = 1;
@@ -250,31 +252,26 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
     } else if (s.v == 48 && ngrads == 2 && vec && block / 2 <= kLdsBudget) {
       // wider teams: dW's block in LDS, dB's accumulators in VGPRs
       s.acc = 3;
-      R = o.rows ? o.rows : r_cap;
-      R = std::max(1, std::min(R, r_cap));
+      R = r_cap;
       s.shmem = block / 2;
     } else {
       // accumulators in VGPRs; LDS only for the final team combine
       s.acc = 0;
-      R = o.rows ? o.rows : r_cap;
-      R = std::max(1, std::min(R, r_cap));
+      R = r_cap;
       while (R > 1 && static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) > kLdsBudget) --R;
       s.shmem = R > 1 ? static_cast<size_t>(R - 1) * s.v * s.team * sizeof(float) : 0;
     }
   } else if (kind == 2) {
     // frozen backward: workgroups of at least four waves
-    R = o.rows ? o.rows : std::max(1, 256 / s.team);
-    R = std::max(1, std::min(R, r_cap));
+    R = std::max(1, std::min(256 / s.team, r_cap));
   } else {
-    R = o.rows ? o.rows : 1;
-    R = std::max(1, std::min(R, r_cap));
+    R = 1;
   }
   s.R = R;
   if (kind == 1) {
     const int64_t groups = cdiv(M, R);
     const int64_t pmax = max_partials(N);
-    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R) : cdiv(groups, pmax) * R;
-    if (cdiv(M, rows) > std::min<int64_t>(M, pmax)) rows = cdiv(groups, pmax) * R;
+    const int64_t rows = cdiv(groups, pmax) * R;
     s.rows_per_wg = std::max<int64_t>(rows, R);
     s.P = static_cast<int>(M > 0 ? cdiv(M, s.rows_per_wg) : 0);
     s.grid = s.P;
@@ -282,8 +279,7 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
     // forward: about kTargetGrid workgroups; frozen backward: one pass per workgroup
     // (short workgroups overlap each other's latency better than a persistent loop
     // without prefetch: 8192 x 8192 bf16 69.8 us against 75.7 at four rows per team)
-    int64_t rows = o.wg_rows ? round_up(o.wg_rows, R)
-                             : (kind == 2 ? R : round_up(cdiv(M, kTargetGrid), R));
+    int64_t rows = kind == 2 ? R : round_up(cdiv(M, kTargetGrid), R);
     // keep the grid within the 2^31 workgroup limit for very tall inputs
     rows = std::max<int64_t>(rows, round_up(cdiv(M, int64_t(1) << 30), R));
     s.rows_per_wg = std::max<int64_t>(rows, R);
@@ -300,7 +296,7 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
 // CU (so at most 128 rows).  The forward and both backward forms take the same
 // decision; in the backward that makes dx come from the same kernel and the same sums
 // with and without parameter gradients.  Needs 16-byte accesses and no output that is
-// also an input; not taken while a launch-shape override is set for the kind.
+// also an input.
 #ifndef RN_SPLIT_MAX_WG
 #define RN_SPLIT_MAX_WG 256
 #endif
@@ -318,10 +314,9 @@ struct Split {
   int spans = 0;       // spans each workgroup writes
   bool group = false;  // a row's workgroups renumbered onto one XCD
 };
-inline Split split_plan(int kind, int op, int64_t M, int64_t N, int eb, bool vec, bool aliased) {
+inline Split split_plan(int op, int64_t M, int64_t N, int eb, bool vec, bool aliased) {
   Split sp;
-  const Override& o = g_override[kind];
-  if (!vec || aliased || o.v || o.rows || o.wg_rows) return sp;
+  if (!vec || aliased) return sp;
   if (M > max_partials(N)) return sp;  // one partial row per row must fit the workspace
   const int64_t ns = cdiv(N, static_cast<int64_t>(SPLIT_WG) * (16 / eb));
   const int64_t g = std::min<int64_t>(ns, RN_SPLIT_MAX_WG / M);
@@ -335,16 +330,27 @@ inline Split split_plan(int kind, int op, int64_t M, int64_t N, int eb, bool vec
   return sp;
 }
 
-inline int launched() { return hipGetLastError() == hipSuccess ? RN_OK : RN_ERR_HIP; }
+// Instrumentation (rn_instrument.h): per-thread dispatch timing events, [kernel][start,
+// stop]; kernel 0 = forward, 1 = the backward's first kernel.
+thread_local hipEvent_t t_timing[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
 
+inline int status_of(int ls) {
+  return ls == LS_OK ? RN_OK : (ls == LS_HIP ? RN_ERR_HIP : RN_ERR_INTERNAL);
+}
+
+// Stage 2: the column sum of the partial rows (for M = 0: zero parameter gradients).
 int colsum(const float* ws, int64_t ldws, int P, int64_t N, float* o0, float* o1,
            hipStream_t st) {
   const int n_out = (o0 != nullptr) + (o1 != nullptr);
   if (n_out == 0) return RN_OK;
-  dim3 grid(static_cast<unsigned>(cdiv(N, CS_C4 * 4)), n_out);
-  colsum_kernel<<<grid, CS_THREADS, 0, st>>>(ws, ldws, P, static_cast<int>(N),
-                                             o0 != nullptr ? o0 : o1, o1);
-  return launched();
+  const dim3 grid(static_cast<unsigned>(cdiv(N, CS_C4 * 4)), n_out);
+  int n = static_cast<int>(N);
+  float* first = o0 != nullptr ? o0 : o1;
+  void* args[] = {&ws, &ldws, &P, &n, &first, &o1};
+  return hipLaunchKernel(reinterpret_cast<const void*>(colsum_kernel), grid, dim3(CS_THREADS), args,
+                         0, st) == hipSuccess
+             ? RN_OK
+             : RN_ERR_HIP;
 }
 
 }  // namespace
@@ -367,27 +373,15 @@ const char* rn_status_str(int status) {
     case RN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case RN_ERR_HIP: return "kernel launch failed";
     case RN_ERR_ALIAS: return "two outputs share storage";
+    case RN_ERR_INTERNAL: return "internal error: no compiled kernel instance for this launch";
     default: return "unknown status";
   }
 }
 
-int rn_set_launch_override(int kind, int v, int rows, int wg_rows) {
-  if (kind < 0 || kind > 2 || v < 0 || rows < 0 || wg_rows < 0) return RN_ERR_SHAPE;
-  if (v != 0) {
-    bool known = false;
-    for (int k : kVs) known = known || (k == v);  // unusable sizes fall back to automatic
-    if (!known) return RN_ERR_SHAPE;
-  }
-  g_override[kind].v = v;
-  g_override[kind].rows = rows;
-  g_override[kind].wg_rows = wg_rows;
-  return RN_OK;
-}
-
 int rn_set_timing_events(int kernel, hipEvent_t start, hipEvent_t stop) {
   if (kernel < 0 || kernel > 1) return RN_ERR_SHAPE;
-  g_timing[kernel][0] = start;
-  g_timing[kernel][1] = stop;
+  t_timing[kernel][0] = start;
+  t_timing[kernel][1] = stop;
   return RN_OK;
 }
 
@@ -407,6 +401,8 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   if (op == OP_FADD && M > 1 && (ldr < N || ldro < N)) return RN_ERR_STRIDE;
   if (op == OP_FADD && ro == y) return RN_ERR_ALIAS;
   if ((rstd != nullptr && rstd == mean)) return RN_ERR_ALIAS;
+  if (M == 1) ldx = ldy = ldr = ldro = N;  // one row: its stride is never used (narrow
+                                           // teams past the row must not wrap onto it)
 
   const int eb = elem_bytes(xt);
   const int ve = 16 / eb;
@@ -417,8 +413,8 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   int64_t max_ld = std::max(ldx, ldy);
   if (op == OP_FADD) max_ld = std::max({max_ld, ldr, ldro});
   const bool aliased = y == x || (op == OP_FADD && (y == res || ro == x || ro == res));
-  const Split sp = split_plan(0, op, M, N, eb, vec, aliased);
-  const Shape s = plan(0, op, M, N, xt, 0, vec, M > 1 ? max_ld : N);
+  const Split sp = split_plan(op, M, N, eb, vec, aliased);
+  const Shape s = plan(0, op, M, N, xt, 0, vec, max_ld);
   FwdArgs a{};
   a.x = x; a.ldx = ldx; a.res = res; a.ldr = ldr; a.w = w; a.b = b;
   a.y = y; a.ldy = ldy; a.ro = ro; a.ldro = ldro; a.rstd = rstd; a.mean = mean;
@@ -427,20 +423,19 @@ static int forward(int op, const void* x, int64_t ldx, const void* res, int64_t 
   a.eps = eps; a.offset = offset;
   a.spans_per_wg = sp.spans;
   Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
-           dim3(static_cast<unsigned>(s.R * s.team)), 0, g_timing[0][0], g_timing[0][1]};
+           dim3(static_cast<unsigned>(s.R * s.team)), 0};
+  l.ev_start = t_timing[0][0];
+  l.ev_stop = t_timing[0][1];
   if (sp.wgs > 0) {
     l.split = true;
     l.group = sp.group;
     l.grid = dim3(static_cast<unsigned>(sp.wgs), static_cast<unsigned>(M));
     l.block = dim3(SPLIT_WG);
   }
-  bool ok = false;
   const int dx = to_dt(xt), dw = to_dt(wt);
-  if (op == OP_RMS) ok = launch_fwd_rms(dx, dw, l, a, st);
-  else if (op == OP_LN) ok = launch_fwd_ln(dx, dw, l, a, st);
-  else ok = launch_fwd_fadd(dx, dw, l, a, st);
-  if (!ok) return RN_ERR_DTYPE;
-  return launched();
+  if (op == OP_RMS) return status_of(launch_fwd_rms(dx, dw, l, a, st));
+  if (op == OP_LN) return status_of(launch_fwd_ln(dx, dw, l, a, st));
+  return status_of(launch_fwd_fadd(dx, dw, l, a, st));
 }
 
 int rmsnorm_fwd(const void* x, int64_t ldx, const void* w, void* y, int64_t ldy, float* rstd,
@@ -485,9 +480,11 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
     if (M > 1 && (lddy < N || ldx < N || lddx < N)) return RN_ERR_STRIDE;
     if (dres != nullptr && M > 1 && lddr < N) return RN_ERR_STRIDE;
   }
+  if (M == 1) lddy = ldx = lddx = lddr = N;  // one row: its stride is never used
   const int64_t ldws = ldws_of(N);
+  float* const part = static_cast<float*>(ws);
   if (M == 0) {  // parameter gradients of an empty batch are zero
-    return colsum(static_cast<const float*>(ws), ldws, 0, N, dw, db, st);
+    return colsum(part, ldws, 0, N, dw, db, st);
   }
 
   const int eb = elem_bytes(xt);
@@ -499,18 +496,17 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   if (dres != nullptr) max_ld = std::max(max_ld, lddr);
   const int kind = ngrads > 0 ? 1 : 2;
   const bool aliased = dx == dy || dx == x || (dres != nullptr && dx == dres);
-  const Split sp = split_plan(kind, op, M, N, eb, vec, aliased);
-  const Shape s = plan(kind, op, M, N, xt, ngrads, vec, M > 1 ? max_ld : N);
+  const Split sp = split_plan(op, M, N, eb, vec, aliased);
+  const Shape s = plan(kind, op, M, N, xt, ngrads, vec, max_ld);
   // partial rows: one per workgroup, or one per row when rows are split
   const int P = sp.wgs > 0 ? static_cast<int>(M) : s.P;
   BwdArgs a{};
   a.dy = dy; a.lddy = lddy; a.x = x; a.ldx = ldx; a.dres = dres; a.lddr = lddr; a.w = w;
   a.dx = dx; a.lddx = lddx;
   // One partial row in all (a decode row, say): it is the gradient itself, written in
-  // place of a partial row, and no column sum is launched.  The kernels write 16-byte
-  // groups, so this needs 16-byte aligned outputs.
+  // place of a partial row, and no column sum runs.  The kernels write 16-byte groups,
+  // so this needs 16-byte aligned outputs.
   const bool direct = P == 1 && aligned16(dw) && aligned16(db);
-  float* const part = static_cast<float*>(ws);
   a.pw = direct ? dw : part;
   a.pb = direct ? db : part + (dw != nullptr ? static_cast<int64_t>(P) * ldws : 0);
   a.ldws = ldws;
@@ -519,7 +515,9 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   a.eps = eps; a.offset = offset;
   a.spans_per_wg = sp.spans;
   Launch l{s.v, vec, s.ts, dim3(static_cast<unsigned>(s.grid)),
-           dim3(static_cast<unsigned>(s.R * s.team)), s.shmem, g_timing[1][0], g_timing[1][1]};
+           dim3(static_cast<unsigned>(s.R * s.team)), s.shmem};
+  l.ev_start = t_timing[1][0];
+  l.ev_stop = t_timing[1][1];
   if (sp.wgs > 0) {
     l.split = true;
     l.group = sp.group;
@@ -527,18 +525,17 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
     l.block = dim3(SPLIT_WG);
     l.shmem = 0;
   }
-  bool ok = false;
   const int dxt = to_dt(xt), dwt = to_dt(wt);
   // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it
   const bool xg = (wt != RN_F32) && (op == OP_LN || offset == 0.0f);
   const BwdVariant bv{dw != nullptr, db != nullptr, xg, s.acc};
-  if (op == OP_RMS) ok = launch_bwd_rms(dxt, dwt, bv, l, a, st);
-  else if (op == OP_LN) ok = launch_bwd_ln(dxt, dwt, bv, l, a, st);
-  else ok = launch_bwd_fadd(dxt, dwt, bv, l, a, st);
-  if (!ok) return RN_ERR_DTYPE;
-  if ((e = launched()) != RN_OK) return e;
+  int ls;
+  if (op == OP_RMS) ls = launch_bwd_rms(dxt, dwt, bv, l, a, st);
+  else if (op == OP_LN) ls = launch_bwd_ln(dxt, dwt, bv, l, a, st);
+  else ls = launch_bwd_fadd(dxt, dwt, bv, l, a, st);
+  if ((e = status_of(ls)) != RN_OK) return e;
   if (ngrads == 0 || direct) return RN_OK;  // frozen, or the gradient written directly
-  return colsum(static_cast<const float*>(ws), ldws, P, N, dw, db, st);
+  return colsum(part, ldws, P, N, dw, db, st);
 }
 
 int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, void* dx,

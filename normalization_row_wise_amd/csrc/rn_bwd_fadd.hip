@@ -2,14 +2,14 @@
 #include "rn_launch.h"
 
 namespace rn {
-bool launch_bwd_fadd(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
-                    hipStream_t s) {
+int launch_bwd_fadd(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
+                   hipStream_t s) {
 #define RN_PAIR(X, W)                                                           \
   if (dx == X && dw == W)                                                       \
     return b.cdw ? bwd_flags<OP_FADD, X, W, true, false>(b, l, a, s)             \
                  : bwd_flags<OP_FADD, X, W, false, false>(b, l, a, s);
   RN_FOR_TYPE_PAIRS(RN_PAIR)
 #undef RN_PAIR
-  return false;
+  return LS_NO_INSTANCE;
 }
 }  // namespace rn

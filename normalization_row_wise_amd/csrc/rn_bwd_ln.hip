@@ -2,7 +2,7 @@
 #include "rn_launch.h"
 
 namespace rn {
-bool launch_bwd_ln(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
+int launch_bwd_ln(int dx, int dw, const BwdVariant& b, const Launch& l, const BwdArgs& a,
                    hipStream_t s) {
 #define RN_PAIR(X, W)                                                                  \
   if (dx == X && dw == W) {                                                            \
@@ -13,6 +13,6 @@ bool launch_bwd_ln(int dx, int dw, const BwdVariant& b, const Launch& l, const B
   }
   RN_FOR_TYPE_PAIRS(RN_PAIR)
 #undef RN_PAIR
-  return false;
+  return LS_NO_INSTANCE;
 }
 }  // namespace rn

@@ -2,10 +2,10 @@
 #include "rn_launch.h"
 
 namespace rn {
-bool launch_fwd_ln(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s) {
+int launch_fwd_ln(int dx, int dw, const Launch& l, const FwdArgs& a, hipStream_t s) {
 #define RN_PAIR(X, W) if (dx == X && dw == W) return fwd_v<OP_LN, X, W>(l, a, s);
   RN_FOR_TYPE_PAIRS(RN_PAIR)
 #undef RN_PAIR
-  return false;
+  return LS_NO_INSTANCE;
 }
 }  // namespace rn

@@ -530,7 +530,10 @@ __global__ __launch_bounds__(bwd_max_wg(V, Ty<DX>::B)) void bwd_kernel(BwdArgs p
   static_assert(ACC != 2 || (V == 48 && TS == 0), "the 384-stride blocks are for V = 48");
   static_assert(ACC != 3 || (CDW && CDB && TS == 0), "split homes are for dW and dB");
   __shared__ double red[2][16][4];
-  extern __shared__ float part[];
+  // dynamic LDS (accumulator blocks, team combine, reducer tree), accessed as 16-byte
+  // groups: declared as float4 so that it starts 16-byte aligned after the static slots
+  extern __shared__ float4 part_lds[];
+  float* const part = reinterpret_cast<float*>(part_lds);
   int parity = 0;
   const int T = TS > 0 ? TS : p.team;
   const int tid = threadIdx.x;

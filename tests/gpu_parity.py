@@ -10,6 +10,7 @@ Gates (the tolerances this path is held to):
   * rstd / mean (fp32): relative L2 <= 1e-6.
   * residual_out: bit-exact (x + residual of two stored values, rounded once).
   * dx with frozen parameters: bit-identical to dx with trainable parameters.
+Every row of every output is compared (check() runs the oracle on chunks of rows).
 Relative L2 is ||a - o||_2 / max(||o||_2, 1e-30) in fp64 (the metric of the accuracy
 reproduction on "fix(cutedsl): fuse Gemma RMSNorm weight offset in FP32").
 """
@@ -45,15 +46,30 @@ def gpu_bits(t: torch.Tensor, dt: str) -> np.ndarray:
     return t.detach().contiguous().view(_BITS_VIEW[dt]).cpu().numpy().view(_NP_BITS[dt])
 
 
-def io_report(t: torch.Tensor, ref: np.ndarray, dt: str) -> dict:
-    """Compare a stored GPU tensor of type dt with the fp64 oracle value."""
+def io_stats(t: torch.Tensor, ref: np.ndarray, dt: str) -> np.ndarray:
+    """Additive comparison statistics of a stored GPU tensor of type dt against the
+    fp64 oracle value rounded once to dt: [sum (g - r)^2, sum r^2, max ulp distance,
+    elements more than 1 ulp away, NaNs] (sums combine over row chunks; max by max)."""
     gb = gpu_bits(t, dt)
     r = oracle.round_to(ref, dt)
     rb = oracle.to_bits(r, dt)
     ulp = oracle.ulp_distance(gb, rb, dt)
-    g = oracle.from_bits(gb, dt)
-    return {"rel_l2": rel_l2(g, r), "max_ulp": int(ulp.max()) if ulp.size else 0,
-            "n_ulp_gt1": int((ulp > 1).sum()), "nan": int(np.isnan(g).sum())}
+    g = oracle.from_bits(gb, dt).astype(np.float64).ravel()
+    r = np.asarray(r, np.float64).ravel()
+    d = g - r
+    return np.array([float(np.dot(d, d)), float(np.dot(r, r)),
+                     float(ulp.max()) if ulp.size else 0.0, float((ulp > 1).sum()),
+                     float(np.isnan(g).sum())])
+
+
+def _report(st: np.ndarray) -> dict:
+    return {"rel_l2": float(np.sqrt(st[0]) / max(np.sqrt(st[1]), 1e-30)), "max_ulp": int(st[2]),
+            "n_ulp_gt1": int(st[3]), "nan": int(st[4])}
+
+
+def io_report(t: torch.Tensor, ref: np.ndarray, dt: str) -> dict:
+    """Compare a stored GPU tensor of type dt with the fp64 oracle value."""
+    return _report(io_stats(t, ref, dt))
 
 
 def io_ok(rep: dict, dt: str) -> bool:
@@ -75,33 +91,45 @@ def to_device(tensors: dict) -> dict:
     return out
 
 
-def run_gpu(wl: workloads.Workload, t: dict, *, dw: bool = True, db: bool = True) -> dict:
-    """Forward then backward on the GPU; returns CPU copies of every output."""
+def run_gpu(wl: workloads.Workload, t: dict, *, dw: bool = True, db: bool = True,
+            inplace: bool = False) -> dict:
+    """Forward then backward on the GPU; returns CPU copies of every output.  inplace:
+    y overwrites (a copy of) x, residual_out a copy of the residual, dx a copy of dy."""
     import normalization_row_wise_amd as rn
     d = to_device(t)
     out = {}
     if wl.op == "rmsnorm":
-        y, rstd = rn.rmsnorm_fwd(d["x"], d["w"], d["eps"], d["offset"])
-        dx, dw_ = rn.rmsnorm_bwd(d["dy"], d["x"], d["w"], d["eps"], d["offset"],
-                                 dw=True if dw else None)
+        xin = d["x"].clone() if inplace else d["x"]
+        y, rstd = rn.rmsnorm_fwd(xin, d["w"], d["eps"], d["offset"], y=xin if inplace else None)
+        dy = d["dy"].clone() if inplace else d["dy"]
+        dx, dw_ = rn.rmsnorm_bwd(dy, d["x"], d["w"], d["eps"], d["offset"],
+                                 dx=dy if inplace else None, dw=True if dw else None)
         out.update(y=y, rstd=rstd, dx=dx, dw=dw_)
     elif wl.op == "layernorm":
-        y, mean, rstd = rn.layernorm_fwd(d["x"], d["w"], d.get("b"), d["eps"])
-        dx, dw_, db_ = rn.layernorm_bwd(d["dy"], d["x"], d["w"], d["eps"],
+        xin = d["x"].clone() if inplace else d["x"]
+        y, mean, rstd = rn.layernorm_fwd(xin, d["w"], d.get("b"), d["eps"],
+                                         y=xin if inplace else None)
+        dy = d["dy"].clone() if inplace else d["dy"]
+        dx, dw_, db_ = rn.layernorm_bwd(dy, d["x"], d["w"], d["eps"], dx=dy if inplace else None,
                                         dw=True if dw else None, db=True if db else None)
         out.update(y=y, mean=mean, rstd=rstd, dx=dx, dw=dw_, db=db_)
     else:
-        y, ro, rstd = rn.fused_add_rmsnorm_fwd(d["x"], d["residual"], d["w"], d["eps"], d["offset"])
-        dx, dw_ = rn.fused_add_rmsnorm_bwd(d["dy"], ro, d["w"], d["eps"], d["offset"],
-                                           d.get("dres"), dw=True if dw else None)
+        res = d["residual"].clone() if inplace else d["residual"]
+        y, ro, rstd = rn.fused_add_rmsnorm_fwd(d["x"], res, d["w"], d["eps"], d["offset"],
+                                               residual_out=res if inplace else None)
+        dy = d["dy"].clone() if inplace else d["dy"]
+        dx, dw_ = rn.fused_add_rmsnorm_bwd(dy, ro, d["w"], d["eps"], d["offset"],
+                                           d.get("dres"), dx=dy if inplace else None,
+                                           dw=True if dw else None)
         out.update(y=y, residual_out=ro, rstd=rstd, dx=dx, dw=dw_)
     torch.cuda.synchronize()
     return {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
 
 
-def run_oracle(wl: workloads.Workload, t: dict, rows=None) -> dict:
-    """The oracle on the same inputs (optionally only on a subset of rows; then no
-    parameter gradients, which need every row)."""
+def run_oracle(wl: workloads.Workload, t: dict, rows=None, keep_grads: bool = False) -> dict:
+    """The oracle on the same inputs, optionally only on a subset of rows.  For a subset
+    the parameter gradients (sums over every row) are dropped, unless keep_grads: then
+    they are the subset's own column sums (chunks of rows add up to the whole)."""
     f = workloads.as_f64
     sel = (lambda a: a) if rows is None else (lambda a: a[rows])
     x, dy, w = sel(f(t["x"])), sel(f(t["dy"])), f(t["w"])
@@ -121,7 +149,7 @@ def run_oracle(wl: workloads.Workload, t: dict, rows=None) -> dict:
         dres = sel(f(t["dres"])) if "dres" in t else None
         out["dx"], out["dw"] = oracle.fused_add_rmsnorm_bwd(dy, dres, out["residual_out"], w, eps,
                                                             off)
-    if rows is not None:
+    if rows is not None and not keep_grads:
         out.pop("dw", None)
         out.pop("db", None)
     return out
@@ -151,22 +179,62 @@ def compare(wl: workloads.Workload, g: dict, o: dict, rows=None) -> list[str]:
     return fails
 
 
-def check(wl: workloads.Workload, sample_rows: int | None = None) -> list[str]:
+# Rows per oracle chunk in check(): about 4 Mi elements (fp64 temporaries of a few
+# tens of MB), so that every row of the largest workloads is compared.
+CHUNK_ELEMS = 1 << 22
+
+
+def compare_all_rows(wl: workloads.Workload, g: dict, t: dict) -> list[str]:
+    """compare() over every row of the workload, running the oracle on chunks of rows:
+    per-element gates on all M rows, relative L2 over the whole tensors, and dw / db
+    against the sum of the chunks' column sums (fp64)."""
+    M = wl.M
+    chunk = max(1, CHUNK_ELEMS // wl.N)
+    io, stat, grads = {}, {}, {}
+    for r0 in range(0, max(M, 1), chunk):
+        rows = slice(r0, min(M, r0 + chunk))
+        o = run_oracle(wl, t, rows, keep_grads=True)
+        for k in ("y", "dx", "residual_out"):
+            if k in o:
+                st = io_stats(g[k][rows], o[k], wl.io)
+                if k in io:
+                    io[k][[0, 1, 3, 4]] += st[[0, 1, 3, 4]]
+                    io[k][2] = max(io[k][2], st[2])
+                else:
+                    io[k] = st
+        for k in ("rstd", "mean"):
+            if k in o and g.get(k) is not None:
+                a = g[k][rows].double().numpy()
+                dd = a - o[k]
+                stat[k] = stat.get(k, np.zeros(2)) + [float(np.dot(dd, dd)),
+                                                      float(np.dot(o[k], o[k]))]
+        for k in ("dw", "db"):
+            if k in o:
+                grads[k] = grads.get(k, 0.0) + o[k]
+    fails = []
+    for k, st in io.items():
+        rep = _report(st)
+        if not io_ok(rep, wl.io):
+            fails.append(f"{wl.name} {k}: {rep}")
+        if k == "residual_out" and rep["max_ulp"] != 0:
+            fails.append(f"{wl.name} residual_out not bit-exact: {rep}")
+    for k, (sd, sr) in stat.items():
+        e = float(np.sqrt(sd) / max(np.sqrt(sr), 1e-30))
+        if not e <= REL_STAT:
+            fails.append(f"{wl.name} {k}: rel_l2 {e:.3e}")
+    for k, ref in grads.items():
+        if g.get(k) is not None:
+            e = f32_report(g[k], ref)
+            if not e <= REL_GRAD:
+                fails.append(f"{wl.name} {k}: rel_l2 {e:.3e}")
+    return fails
+
+
+def check(wl: workloads.Workload) -> list[str]:
+    """Forward + backward on the GPU against the oracle, every row compared."""
     t = workloads.generate(wl)
     g = run_gpu(wl, t)
-    rows = None
-    if sample_rows is not None and wl.M > sample_rows:
-        rows = np.sort(np.random.default_rng(1).choice(wl.M, sample_rows, replace=False))
-    o = run_oracle(wl, t, rows)
-    fails = compare(wl, g, o, rows)
-    if rows is not None:  # parameter gradients need every row
-        o_full = run_oracle(wl, t)
-        for k in ("dw", "db"):
-            if k in o_full and g.get(k) is not None:
-                e = f32_report(g[k], o_full[k])
-                if not e <= REL_GRAD:
-                    fails.append(f"{wl.name} {k}: rel_l2 {e:.3e}")
-    return fails
+    return compare_all_rows(wl, g, t)
 
 
 def smoke_check() -> None:

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(rn):
     assert not missing, missing
 
 
-RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 F32, F16, BF16 = 0, 1, 2
 P = ctypes.c_void_p(4096)    # a non-null address that is never dereferenced
 Q = ctypes.c_void_p(8192)
@@ -51,7 +51,7 @@ S = ctypes.c_void_p(16384)
 
 
 def test_status_strings(rn):
-    for code in (RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS):
+    for code in (RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT):
         s = rn.lib.rn_status_str(code).decode()
         assert s and s != "unknown status"
     assert rn.lib.rn_status_str(42).decode() == "unknown status"
@@ -64,6 +64,8 @@ def test_workspace_query(rn):
     one = ws(2048, 4096, 1)
     assert one > 0 and ws(2048, 4096, 2) == 2 * one
     assert one % 16 == 0 and one >= 4096 * 4
+    assert one == 256 * 4096 * 4               # at most 256 partial rows of N fp32
+    assert ws(3, 100, 1) == 3 * 128 * 4   # rows padded to 64 floats
     assert ws(8192, 8192, 1) >= ws(2048, 4096, 1)
     assert ws(-1, 4096, 1) == 0 and ws(4, 0, 1) == 0 and ws(4, 10**6, 1) == 0
     assert ws(4, 64, 3) == 0
@@ -115,12 +117,20 @@ def test_backward_argument_errors(rn):
               None) == E_STRIDE                                    # dres_out stride
 
 
-def test_launch_override_validation(rn):
-    L = rn.lib
-    assert L.rn_set_launch_override(3, 0, 0, 0) == E_SHAPE
-    assert L.rn_set_launch_override(0, 12, 0, 0) == E_SHAPE       # not a compiled V
-    assert L.rn_set_launch_override(0, 16, 2, 0) == RN_OK
-    assert L.rn_set_launch_override(0, 0, 0, 0) == RN_OK          # back to automatic
+def test_no_process_wide_tuning_state(rn):
+    """The product ABI holds no tuning state: no launch-shape override exists, and the
+    one instrumentation hook (dispatch timing events, per calling thread) is declared
+    only in the internal instrumentation header, not in include/rownorm.h."""
+    lib = ctypes.CDLL(rn.LIB_PATH)
+    assert not hasattr(lib, "rn_set_launch_override")
+    assert "rn_set_timing_events" not in declared_functions()
+    internal = open(os.path.join(ROOT, "normalization_row_wise_amd", "csrc",
+                                 "rn_instrument.h")).read()
+    assert "int rn_set_timing_events(" in internal and "thread" in internal
+    src = open(os.path.join(ROOT, "normalization_row_wise_amd", "csrc", "rn_abi.hip")).read()
+    assert "thread_local hipEvent_t t_timing" in src
+    assert lib.rn_set_timing_events(2, None, None) == E_SHAPE
+    assert lib.rn_set_timing_events(0, None, None) == RN_OK
 
 
 def test_binding_refuses_host_tensors(rn):

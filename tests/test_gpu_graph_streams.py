@@ -59,7 +59,7 @@ class Problem:
                 self.out["db"] = torch.empty(N, **f32)
                 ngr = 2
         need = rn.workspace_bytes(M, N, ngr) if ngr else 0
-        self.ws = torch.empty(need, dtype=torch.uint8, device=gp.dev()) if need else None
+        self.ws = rn.new_workspace(need, gp.dev()) if need else None
 
     def refill(self, seed):
         w = self.wl

@@ -53,7 +53,7 @@ def test_narrow_rows(wl):
 @pytest.mark.parametrize("wl", workloads.EXTRAS, ids=lambda c: c.name)
 def test_narrow_named_workload(wl):
     _say(wl.name)
-    fails = gp.check(wl, sample_rows=2048)
+    fails = gp.check(wl)
     assert not fails, "\n".join(fails)
 
 

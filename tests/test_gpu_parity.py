@@ -35,13 +35,12 @@ FULL = [c for c in workloads.CONFIGS]
 @pytest.mark.parametrize("wl", FULL, ids=lambda c: c.name)
 def test_named_workload(wl):
     _say(wl.name)
-    sample = 512 if wl.M * wl.N > 16 * 2**20 else None
-    fails = gp.check(wl, sample_rows=sample)
+    fails = gp.check(wl)
     assert not fails, "\n".join(fails)
 
 
 # Maximum sizes: a million rows of 8 (the narrow path's grid-stride limits) and rows of
-# the widest N at thousands of rows; outputs checked on sampled rows, dW / dB in full.
+# the widest N at thousands of rows; every row compared.
 LARGE = [
     workloads.small("rmsnorm", 2**20 + 3, 8, "bf16", offset=1.0, weight="gemma", seed=71),
     workloads.small("layernorm", 3001, 24576, "bf16", seed=72),
@@ -52,7 +51,7 @@ LARGE = [
 @pytest.mark.parametrize("wl", LARGE, ids=lambda c: c.name)
 def test_largest_shapes(wl):
     _say(wl.name)
-    fails = gp.check(wl, sample_rows=1024)
+    fails = gp.check(wl)
     assert not fails, "\n".join(fails)
 
 
@@ -167,7 +166,7 @@ WIDE_PF = [
 @pytest.mark.parametrize("wl", WIDE_PF, ids=lambda c: c.name)
 def test_wide_rows_one_row_ahead(wl):
     _say("wide prefetch", wl.name)
-    fails = gp.check(wl, sample_rows=512)
+    fails = gp.check(wl)
     assert not fails, "\n".join(fails)
     t = workloads.generate(wl)
     full = gp.run_gpu(wl, t, dw=True, db=True)
@@ -195,7 +194,7 @@ RMS_TALL = [
 @pytest.mark.parametrize("wl", RMS_TALL, ids=lambda c: c.name)
 def test_tall_rows_small_workgroups(wl):
     _say("tall rows", wl.name)
-    fails = gp.check(wl, sample_rows=512)
+    fails = gp.check(wl)
     assert not fails, "\n".join(fails)
     t = workloads.generate(wl)
     full = gp.run_gpu(wl, t, dw=True, db=True)
