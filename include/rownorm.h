@@ -80,7 +80,9 @@ typedef enum rn_status {
   RN_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than rn_bwd_workspace_bytes */
   RN_ERR_HIP = -6,        /* a kernel launch failed                                */
   RN_ERR_ALIAS = -7,      /* two outputs share storage                             */
-  RN_ERR_INTERNAL = -8    /* no compiled kernel instance for the planned launch    */
+  RN_ERR_INTERNAL = -8,   /* no compiled kernel instance for the planned launch    */
+  RN_ERR_SCRATCH = -9     /* rmsnorm_bwd_noalloc: the shape needs more partial-row */
+                          /* space than its fixed scratch holds                    */
 } rn_status;
 
 #define RN_MAX_N 24576
@@ -118,6 +120,21 @@ int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const 
                 void* dx, int64_t lddx, float* dw, void* ws, size_t ws_bytes,
                 int64_t M, int64_t N, float eps, float offset,
                 rn_dtype xt, rn_dtype wt, hipStream_t stream);
+
+/* RMSNorm backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate (code under hipGraph capture without a memory pool, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and contract as
+ * rmsnorm_bwd without ws / ws_bytes: the partial rows of dw live in a device array
+ * inside the library, one per GPU (8 MiB, held until the process ends; its address is
+ * looked up once per device).  Limit: rn_bwd_workspace_bytes(M, N, 1) <= 8 MiB, i.e.
+ * every shape with N <= 8192, and wider rows while min(M, 256) partial rows fit; a
+ * larger call returns RN_ERR_SCRATCH before anything is enqueued.  dw == NULL (frozen)
+ * has no limit.  Calls on one GPU share the array: calls that may overlap in time
+ * (different streams without ordering) race and must not be made. */
+int rmsnorm_bwd_noalloc(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                        const void* w, void* dx, int64_t lddx, float* dw, int64_t M,
+                        int64_t N, float eps, float offset, rn_dtype xt, rn_dtype wt,
+                        hipStream_t stream);
 
 /* LayerNorm forward.  [frozen] Key Changes (LayerNorm with weight and bias).
  *   x in, w [N] in, b [N] in or NULL (no bias), y out, mean / rstd [M] fp32 out or

@@ -29,6 +29,8 @@ _SIGS = {
     "rmsnorm_fwd": (_i32, [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _f32, _f32, _i32, _i32, _vp]),
     "rmsnorm_bwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _i64, _i64, _f32,
                            _f32, _i32, _i32, _vp]),
+    "rmsnorm_bwd_noalloc": (_i32, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _f32,
+                                   _f32, _i32, _i32, _vp]),
     "layernorm_fwd": (_i32, [_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _f32, _i32, _i32,
                              _vp]),
     "layernorm_bwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _i64, _i64,
@@ -171,6 +173,20 @@ def rmsnorm_bwd(dy, x, w, eps: float = 1e-6, offset: float = 0.0, *, dx=None, dw
     return dx, dw
 
 
+def rmsnorm_bwd_noalloc(dy, x, w, eps: float = 1e-6, offset: float = 0.0, *, dx=None, dw=True,
+                        stream=None):
+    """rmsnorm_bwd without a workspace: the library keeps the partial rows of dw in its
+    own per-GPU scratch (8 MiB).  Returns (dx, dw)."""
+    M, N = x.shape
+    dx = torch.empty_like(x, memory_format=torch.contiguous_format) if dx is None else dx
+    if dw is True:
+        dw = torch.empty(N, dtype=torch.float32, device=x.device)
+    _check(lib.rmsnorm_bwd_noalloc(_ptr(dy), _rows(dy, "dy"), _ptr(x), _rows(x, "x"), _ptr(w),
+                                   _ptr(dx), _rows(dx, "dx"), _ptr(dw), M, N, eps, offset, _dt(x),
+                                   _dt(w), _stream(stream)))
+    return dx, dw
+
+
 def layernorm_fwd(x, w, b=None, eps: float = 1e-5, *, y=None, mean=True, rstd=True, stream=None):
     """y = (x - mean) * rstd * w + b.  Returns (y, mean, rstd)."""
     M, N = x.shape
@@ -234,6 +250,6 @@ def fused_add_rmsnorm_bwd(dy, residual_out, w, eps: float = 1e-6, offset: float 
 
 __all__ = [
     "lib", "LIB_PATH", "RowNormError", "workspace_bytes", "new_workspace",
-    "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+    "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc", "layernorm_fwd", "layernorm_bwd",
     "fused_add_rmsnorm_fwd", "fused_add_rmsnorm_bwd",
 ]

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/rownorm.h"
 #include "rn_instrument.h"
@@ -353,6 +354,41 @@ int colsum(const float* ws, int64_t ldws, int P, int64_t N, float* o0, float* o1
              : RN_ERR_HIP;
 }
 
+// ------------------------------------------------------------- no-allocation backward
+// rmsnorm_bwd_noalloc keeps its partial rows of dW in this file-scope device array
+// instead of a caller's workspace: every GPU the library runs on holds one copy of
+// kScratchBytes until the process ends.  Host code uses the array only through the
+// device address hipGetSymbolAddress returns for the current device (the name itself is
+// a host-side stand-in).  Nothing in it needs to start at zero: every partial row a call
+// reads is written earlier in the same call.  Calls that overlap on one GPU (different
+// streams without ordering) share the array and race.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};  // device address of `scratch` per device, set once
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch` (looked up on the first call on a device,
+// with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RN_ERR_HIP;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return RN_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return RN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +410,8 @@ const char* rn_status_str(int status) {
     case RN_ERR_HIP: return "kernel launch failed";
     case RN_ERR_ALIAS: return "two outputs share storage";
     case RN_ERR_INTERNAL: return "internal error: no compiled kernel instance for this launch";
+    case RN_ERR_SCRATCH:
+      return "the no-allocation backward needs more than its fixed scratch (8 MiB of partial rows)";
     default: return "unknown status";
   }
 }
@@ -543,6 +581,21 @@ int rmsnorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const 
                 float offset, rn_dtype xt, rn_dtype wt, hipStream_t stream) {
   return backward(OP_RMS, dy, lddy, x, ldx, nullptr, 0, w, dx, lddx, dw, nullptr, ws, ws_bytes, M,
                   N, eps, offset, xt, wt, stream);
+}
+
+int rmsnorm_bwd_noalloc(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w,
+                        void* dx, int64_t lddx, float* dw, int64_t M, int64_t N, float eps,
+                        float offset, rn_dtype xt, rn_dtype wt, hipStream_t stream) {
+  if (dw == nullptr)  // frozen weight: no partial rows, nothing to hold
+    return backward(OP_RMS, dy, lddy, x, ldx, nullptr, 0, w, dx, lddx, nullptr, nullptr, nullptr, 0,
+                    M, N, eps, offset, xt, wt, stream);
+  int e = check_shape(M, N);
+  if (e != RN_OK) return e;
+  if (rn_bwd_workspace_bytes(M, N, 1) > kScratchBytes) return RN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((e = scratch_address(&ws)) != RN_OK) return e;
+  return backward(OP_RMS, dy, lddy, x, ldx, nullptr, 0, w, dx, lddx, dw, nullptr, ws, kScratchBytes,
+                  M, N, eps, offset, xt, wt, stream);
 }
 
 int layernorm_bwd(const void* dy, int64_t lddy, const void* x, int64_t ldx, const void* w, void* dx,

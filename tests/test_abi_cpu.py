@@ -42,7 +42,8 @@ def test_library_exports_every_declared_symbol(rn):
     assert not missing, missing
 
 
-RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT = 0, -1, -2, -3, -4, -5, -6, -7, -8
+RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT, E_SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 F32, F16, BF16 = 0, 1, 2
 P = ctypes.c_void_p(4096)    # a non-null address that is never dereferenced
 Q = ctypes.c_void_p(8192)
@@ -51,7 +52,7 @@ S = ctypes.c_void_p(16384)
 
 
 def test_status_strings(rn):
-    for code in (RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT):
+    for code in (RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT, E_SCRATCH):
         s = rn.lib.rn_status_str(code).decode()
         assert s and s != "unknown status"
     assert rn.lib.rn_status_str(42).decode() == "unknown status"
@@ -115,6 +116,17 @@ def test_backward_argument_errors(rn):
               None) == E_NULL                                      # residual_out missing
     assert fa(P, 64, Q, 8, Q, 64, Rr, S, 64, None, None, 0, 4, 64, 1e-6, 1.0, BF16, BF16,
               None) == E_STRIDE                                    # dres_out stride
+
+
+def test_noalloc_refuses_before_any_hip_call(rn):
+    """rmsnorm_bwd_noalloc checks the shape and its fixed scratch (8 MiB of partial rows)
+    before touching the GPU: these return without a device present."""
+    f = rn.lib.rmsnorm_bwd_noalloc
+    assert f(P, 16384, Q, 16384, Rr, S, 16384, P, 4096, 16384, 1e-6, 0.0, BF16, BF16,
+             None) == E_SCRATCH                                   # 256 x 64 KiB partial rows
+    assert f(P, 64, Q, 64, Rr, S, 64, P, -1, 64, 1e-6, 0.0, BF16, BF16, None) == E_SHAPE
+    assert f(P, 64, Q, 64, Rr, S, 64, P, 4, 99999, 1e-6, 0.0, BF16, BF16, None) == E_SHAPE
+    assert rn.workspace_bytes(8192, 8192, 1) <= 8 << 20 < rn.workspace_bytes(4096, 16384, 1)
 
 
 def test_no_process_wide_tuning_state(rn):
