@@ -198,16 +198,27 @@ def median(a):
     return a[n // 2] if n % 2 else 0.5 * (a[n // 2 - 1] + a[n // 2])
 
 
-def time_rounds(sets, K, W, rounds, torch, seed=0):
+def time_rounds(sets, K, W, rounds, torch, seed=0, eager=False):
     """Per-step device time (us) of each provider: median over `rounds` rounds of one
-    replay of each provider's K-step graph, providers in a shuffled order per round.
-    Returns ({provider: median us/step}, {provider: [us/step per round]}, wall seconds
-    of the timed replays)."""
+    replay of each provider's K-step graph, providers in a shuffled order per round
+    (eager: the K steps launched one by one instead, for profilers that count per
+    dispatch).  Returns ({provider: median us/step}, {provider: [us/step per round]},
+    wall seconds of the timed replays)."""
     for k in range(W):
         sets.step(k, True)
         sets.step(k, False)
     torch.cuda.synchronize()
-    graphs = {p: capture(sets, K, p != "frozen", torch) for p in PROVIDERS}
+
+    class Eager:
+        def __init__(self, trainable):
+            self.trainable = trainable
+
+        def replay(self):
+            for k in range(K):
+                sets.step(k, self.trainable)
+
+    graphs = {p: (Eager(p != "frozen") if eager else capture(sets, K, p != "frozen", torch))
+              for p in PROVIDERS}
     for g in graphs.values():   # one untimed replay each
         g.replay()
     torch.cuda.synchronize()
@@ -386,7 +397,7 @@ def _cpu_model() -> str:
 EXTRA = ("layernorm_2048x4096_bf16", "fused_add_rmsnorm_2048x8192_bf16")
 
 
-def measure(wl, K, W, rounds, rn, torch, event_steps):
+def measure(wl, K, W, rounds, rn, torch, event_steps, eager=False):
     """The protocol above on one workload: providers' median step times, A/A delta,
     per-call kernel times and the step's algorithmic GB/s."""
     probe = Sets(wl, 1, rn, torch)
@@ -394,7 +405,7 @@ def measure(wl, K, W, rounds, rn, torch, event_steps):
     cold = S * probe.bytes_per_set >= 3 * MALL_BYTES
     del probe
     sets = Sets(wl, S, rn, torch)
-    med, per, wall = time_rounds(sets, K, W, rounds, torch)
+    med, per, wall = time_rounds(sets, K, W, rounds, torch, eager=eager)
     ev_t = call_times(sets, event_steps, True, torch)
     ev_f = call_times(sets, event_steps, False, torch)
     abt, abf = alg_bytes(wl, True), alg_bytes(wl, False)
@@ -423,6 +434,8 @@ def main():
     ap.add_argument("--config", default=workloads.RMS_8192x8192.name,
                     choices=sorted(workloads.BY_NAME))
     ap.add_argument("--no-extra", action="store_true", help="skip the extra configurations")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed steps one by one instead of graph replays (counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--event-steps", type=int, default=100)
@@ -456,7 +469,7 @@ def main():
     import normalization_row_wise_amd as rn
 
     wl = workloads.BY_NAME[args.config]
-    m = measure(wl, args.steps, args.warmup, args.rounds, rn, torch, args.event_steps)
+    m = measure(wl, args.steps, args.warmup, args.rounds, rn, torch, args.event_steps, args.eager)
     sets = m["sets"]
     abt = alg_bytes(wl, True)
     ceiling = stream_ceiling(sets, args.event_steps, torch) if "dres" in sets.sets[0] or \
@@ -474,7 +487,7 @@ def main():
             if name == wl.name:
                 continue
             e = measure(workloads.BY_NAME[name], args.steps, args.warmup, args.rounds, rn, torch,
-                        args.event_steps)
+                        args.event_steps, args.eager)
             extra[name] = {
                 "us_per_step": e["us_per_step"], "aa_delta_pct": e["aa_delta_pct"],
                 "gbs": round(e["gbs"], 1), "pct_of_hbm_peak": round(100 * e["gbs"] / HBM_PEAK_GBS, 2),
@@ -502,7 +515,8 @@ def main():
         "data": "synthetic (seeded CPU randn, no dataset)",
         "config": {"workload": wl.name, "op": wl.op, "M": wl.M, "N": wl.N, "io": wl.io,
                    "weight": wl.wt, "trainable_params": True,
-                   "timing": f"median of {args.rounds} shuffled rounds of HIP-graph replays of "
+                   "timing": f"median of {args.rounds} shuffled rounds of "
+                             f"{'eager launches' if args.eager else 'HIP-graph replays'} of "
                              f"{args.steps} steps (providers trainable, frozen, trainable A/A)",
                    "buffer_sets": m["S"], "inputs_cold_in_mall": m["cold"]},
         "pct_of_hbm_peak": round(100 * m["gbs"] / HBM_PEAK_GBS, 2),
