@@ -1,4 +1,5 @@
-"""Correctness oracle (fp64, CPU, numpy) for the row-wise normalisation path.
+"""Correctness oracle (fp64, CPU, numpy) for the row-wise normalisation path and the
+fused linear distillation loss (``oracle.distill``).
 
 TEST INFRASTRUCTURE ONLY.  Imported by the test suite, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py``; never by the product.  It shares no code
