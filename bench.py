@@ -54,7 +54,8 @@ def source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "normalization_row_wise_amd", "csrc")
-    for f in sorted(os.listdir(csrc)) + ["../../../include/rownorm.h"]:
+    for f in sorted(f for f in os.listdir(csrc) if f.startswith("rn_")) + [
+            "../../../include/rownorm.h"]:
         path = os.path.normpath(os.path.join(csrc, f))
         if os.path.isfile(path):
             h.update(open(path, "rb").read())

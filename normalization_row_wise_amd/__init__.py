@@ -39,6 +39,10 @@ _SIGS = {
                                      _i64, _f32, _f32, _i32, _i32, _vp]),
     "fused_add_rmsnorm_bwd": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp,
                                      _sz, _i64, _i64, _f32, _f32, _i32, _i32, _vp]),
+    # include/distill.h
+    "fused_linear_jsd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i32, _i32, _i32]),
+    "fused_linear_jsd": (_i32, [_vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64,
+                                _f32, _f32, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
 }
 
 

@@ -1,0 +1,227 @@
+// dl_abi.hip — the C ABI of the fused linear JSD distillation loss (include/distill.h):
+// argument checks, workspace layout and the chunk loop ([distill], Summary and Details:
+// tokens in chunks, the student head's weight gradient skipped when frozen).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/distill.h"
+#include "dl_kernels.h"
+
+using namespace dl;
+
+namespace {
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Split of the dx product's K (= V) so that it has about 1024 workgroups.
+inline int dx_splits(int64_t chunk, int64_t H) {
+  const int64_t tiles = cdiv(chunk, BM) * cdiv(H, BN);
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, 1024 / std::max<int64_t>(1, tiles))));
+}
+
+// Byte offsets of the workspace parts (each 256-byte aligned); total in `end`.
+struct Layout {
+  size_t zs, zt, gb, wst, dxp, gbt, xst, jt, end;
+  int64_t ldz, vpad, ldk;
+  int splits;
+};
+
+Layout layout(int64_t BT, int64_t H, int64_t V, int64_t chunk, bool dx, bool dw) {
+  Layout L{};
+  const int64_t c = std::min(chunk, std::max<int64_t>(BT, 1));
+  L.ldz = rup(V, 4);
+  L.vpad = rup(V, 8);
+  L.ldk = rup(c, 8);
+  L.splits = dx ? dx_splits(c, H) : 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = static_cast<size_t>(rup(static_cast<int64_t>(o + bytes), 256));
+    return at;
+  };
+  L.zs = take(static_cast<size_t>(c) * L.ldz * 4);
+  L.zt = take(static_cast<size_t>(c) * L.ldz * 4);
+  L.gb = dx ? take(static_cast<size_t>(c) * L.vpad * 2) : 0;
+  L.wst = dx ? take(static_cast<size_t>(H) * L.vpad * 2) : 0;
+  L.dxp = dx ? take(static_cast<size_t>(L.splits) * c * H * 4) : 0;
+  L.gbt = dw ? take(static_cast<size_t>(V) * L.ldk * 2) : 0;
+  L.xst = dw ? take(static_cast<size_t>(H) * L.ldk * 2) : 0;
+  L.jt = take(static_cast<size_t>(std::max<int64_t>(BT, 1)) * 8);
+  L.end = o;
+  return L;
+}
+
+bool valid_sizes(int64_t BT, int64_t H, int64_t Ht, int64_t V, int64_t chunk) {
+  if (BT < 0 || H < 8 || Ht < 8 || V < 1 || chunk < 1) return false;
+  if (H % 8 || Ht % 8) return false;
+  // in-tile byte offsets of the products stay below 2^31: 128 rows of at most 2^22
+  // elements (V padded, H, the input strides)
+  if (V > (int64_t(1) << 22) - 8 || H > (int64_t(1) << 20) || Ht > (int64_t(1) << 20)) return false;
+  if (BT > (int64_t(1) << 31)) return false;
+  // every buffer addressed with 32-bit byte offsets: the weights, a chunk's logits
+  if (V * std::max(H, Ht) * 2 >= (int64_t(1) << 32)) return false;
+  if (std::min(chunk, std::max<int64_t>(BT, 1)) * rup(V, 4) * 4 >= (int64_t(1) << 32)) return false;
+  if (V * H * 4 >= (int64_t(1) << 32)) return false;  // dW
+  return true;
+}
+
+inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename K, typename... Args>
+int launch(K k, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  void* a[] = {&args...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, a, 0, s) == hipSuccess
+             ? RN_OK
+             : RN_ERR_HIP;
+}
+
+// C[M x N] (+)= A[M x K] B[N x K]^T with `splits` K ranges written to slices of C.
+template <int EPI>
+int gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C, int64_t ldc,
+         int64_t split_stride, const uint16_t* bias, int64_t M, int64_t N, int64_t K, int splits,
+         hipStream_t s) {
+  if (M == 0 || N == 0) return RN_OK;
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
+  g.split_stride = split_stride; g.bias = bias;
+  g.M = static_cast<int>(M); g.N = static_cast<int>(N); g.K = static_cast<int>(K);
+  g.k_per_split = static_cast<int>(rup(cdiv(K, splits), BK));
+  g.mt = static_cast<int>(cdiv(M, BM));
+  g.nt = static_cast<int>(cdiv(N, BN));
+  const dim3 grid(static_cast<unsigned>(8 * cdiv(g.nt, 8) * g.mt), 1, static_cast<unsigned>(splits));
+  return launch(gemm_nt_kernel<EPI>, grid, dim3(GT), s, g);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fused_linear_jsd_workspace_bytes(int64_t BT, int64_t H, int64_t Ht, int64_t V,
+                                        int64_t chunk, int want_dx, int want_dw, int want_db) {
+  (void)want_db;
+  if (!valid_sizes(BT, H, Ht, V, chunk)) return 0;
+  return layout(BT, H, V, chunk, want_dx != 0, want_dw != 0).end;
+}
+
+int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const void* bs,
+                     const void* xt, int64_t ldxt, const void* wt, const void* bt, int64_t BT,
+                     int64_t H, int64_t Ht, int64_t V, float beta, float temperature,
+                     int64_t chunk, float* loss, void* dxs, int64_t lddx, float* dws, float* dbs,
+                     void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!valid_sizes(BT, H, Ht, V, chunk)) return RN_ERR_SHAPE;
+  if (!(beta >= 0.0f && beta <= 1.0f) || !(temperature > 0.0f)) return RN_ERR_SHAPE;
+  if (loss == nullptr || ws == nullptr) return RN_ERR_NULL;
+  if (dbs != nullptr && bs == nullptr) return RN_ERR_NULL;
+  const bool want_dx = dxs != nullptr, want_dw = dws != nullptr, want_db = dbs != nullptr;
+  const Layout L = layout(BT, H, V, chunk, want_dx, want_dw);
+  if (ws_bytes < L.end || (reinterpret_cast<uintptr_t>(ws) & 255u)) return RN_ERR_WORKSPACE;
+  if (BT > 0) {
+    if (xs == nullptr || ws_weight == nullptr || xt == nullptr || wt == nullptr) return RN_ERR_NULL;
+    if ((BT > 1 && (ldxs < H || ldxt < Ht)) || (want_dx && BT > 1 && lddx < H))
+      return RN_ERR_STRIDE;
+    if (ldxs % 8 || ldxt % 8 || ldxs > (int64_t(1) << 22) || ldxt > (int64_t(1) << 22))
+      return RN_ERR_STRIDE;
+    if (!a16(xs) || !a16(ws_weight) || !a16(xt) || !a16(wt)) return RN_ERR_STRIDE;
+  }
+  if (want_dw && dws == loss) return RN_ERR_ALIAS;
+
+  char* base = static_cast<char*>(ws);
+  float* zs = reinterpret_cast<float*>(base + L.zs);
+  float* zt = reinterpret_cast<float*>(base + L.zt);
+  uint16_t* gb = want_dx ? reinterpret_cast<uint16_t*>(base + L.gb) : nullptr;
+  uint16_t* wst = want_dx ? reinterpret_cast<uint16_t*>(base + L.wst) : nullptr;
+  float* dxp = want_dx ? reinterpret_cast<float*>(base + L.dxp) : nullptr;
+  uint16_t* gbt = want_dw ? reinterpret_cast<uint16_t*>(base + L.gbt) : nullptr;
+  uint16_t* xst = want_dw ? reinterpret_cast<uint16_t*>(base + L.xst) : nullptr;
+  double* jt = reinterpret_cast<double*>(base + L.jt);
+  const auto* Xs = static_cast<const uint16_t*>(xs);
+  const auto* Ws = static_cast<const uint16_t*>(ws_weight);
+  const auto* Bs = static_cast<const uint16_t*>(bs);
+  const auto* Xt = static_cast<const uint16_t*>(xt);
+  const auto* Wt = static_cast<const uint16_t*>(wt);
+  const auto* Bt = static_cast<const uint16_t*>(bt);
+  auto* Dx = static_cast<uint16_t*>(dxs);
+  int e = RN_OK;
+
+  if (BT == 0) {  // empty batch: loss 0, gradients 0
+    if ((e = launch(loss_sum_kernel, dim3(1), dim3(1024), st, static_cast<const double*>(jt),
+                    int64_t(0), loss)) != RN_OK)
+      return e;
+    if (want_dw && (e = launch(fill_zero_kernel, dim3(static_cast<unsigned>(cdiv(V * H, 256))),
+                               dim3(256), st, dws, V * H)) != RN_OK)
+      return e;
+    if (want_db && (e = launch(fill_zero_kernel, dim3(static_cast<unsigned>(cdiv(V, 256))), dim3(256),
+                               st, dbs, V)) != RN_OK)
+      return e;
+    return RN_OK;
+  }
+
+  // W_s^T [H][vpad] (zero columns past V): the K-contiguous operand of the dx product
+  if (want_dx &&
+      (e = launch(transpose_bf16_kernel<uint16_t>,
+                  dim3(static_cast<unsigned>(cdiv(H, 64)), static_cast<unsigned>(cdiv(L.vpad, 64))),
+                  dim3(256), st, Ws, H, static_cast<int>(V), static_cast<int>(H), wst, L.vpad,
+                  static_cast<int>(L.vpad))) != RN_OK)
+    return e;
+
+  const int64_t C = std::min(chunk, BT);
+  for (int64_t c0 = 0; c0 < BT; c0 += C) {
+    const int64_t cr = std::min(C, BT - c0);
+    // logits of the chunk (fp32; the bias added in the epilogue)
+    if ((e = gemm<EPI_F32>(Xs + c0 * ldxs, ldxs, Ws, H, zs, L.ldz, 0, Bs, cr, V, H, 1, st)) != RN_OK)
+      return e;
+    if ((e = gemm<EPI_F32>(Xt + c0 * ldxt, ldxt, Wt, Ht, zt, L.ldz, 0, Bt, cr, V, Ht, 1, st)) !=
+        RN_OK)
+      return e;
+    // divergence per token and, if any gradient is wanted, dL/dz (bf16 for dx, fp32 in
+    // place of the student logits for dW and db)
+    JsdArgs j{};
+    j.zs = zs; j.zt = zt; j.ldz = L.ldz; j.gb = gb; j.ldg = L.vpad; j.jtok = jt + c0;
+    j.rows = static_cast<int>(cr); j.V = static_cast<int>(V); j.vpad = static_cast<int>(L.vpad);
+    j.beta = beta; j.inv_tau = 1.0f / temperature;
+    j.grad_scale = static_cast<float>(1.0 / (static_cast<double>(temperature) * static_cast<double>(BT)));
+    j.want_grad = want_dx || want_dw || want_db;
+    j.write_f32 = want_dw || want_db;
+    if ((e = launch(jsd_rows_kernel, dim3(static_cast<unsigned>(cr)), dim3(JT), st, j)) != RN_OK)
+      return e;
+    if (want_dx) {
+      // dx[c0 .. c0 + cr) = dz W_s: K = V in `splits` ranges, then their fixed-order sum
+      if ((e = gemm<EPI_F32>(gb, L.vpad, wst, L.vpad, dxp, H, cr * H, nullptr, cr, H, L.vpad,
+                             L.splits, st)) != RN_OK)
+        return e;
+      if ((e = launch(split_sum_bf16_kernel, dim3(static_cast<unsigned>(cdiv(cr * H, 256))),
+                      dim3(256), st, static_cast<const float*>(dxp), cr * H, L.splits,
+                      static_cast<int>(cr), static_cast<int>(H), H, Dx + c0 * lddx, lddx)) != RN_OK)
+        return e;
+    }
+    if (want_dw) {
+      // dW (+)= dz^T x_s: both operands transposed to K (the chunk's tokens) contiguous,
+      // K padded with zeros to a multiple of 8.  Skipped entirely for a frozen weight.
+      const int ck = static_cast<int>(rup(cr, 8));
+      if ((e = launch(transpose_bf16_kernel<float>,
+                      dim3(static_cast<unsigned>(cdiv(V, 64)), static_cast<unsigned>(cdiv(ck, 64))),
+                      dim3(256), st, static_cast<const float*>(zs), L.ldz, static_cast<int>(cr),
+                      static_cast<int>(V), gbt, L.ldk, ck)) != RN_OK)
+        return e;
+      if ((e = launch(transpose_bf16_kernel<uint16_t>,
+                      dim3(static_cast<unsigned>(cdiv(H, 64)), static_cast<unsigned>(cdiv(ck, 64))),
+                      dim3(256), st, Xs + c0 * ldxs, ldxs, static_cast<int>(cr), static_cast<int>(H),
+                      xst, L.ldk, ck)) != RN_OK)
+        return e;
+      e = c0 == 0 ? gemm<EPI_F32>(gbt, L.ldk, xst, L.ldk, dws, H, 0, nullptr, V, H, ck, 1, st)
+                  : gemm<EPI_F32_ADD>(gbt, L.ldk, xst, L.ldk, dws, H, 0, nullptr, V, H, ck, 1, st);
+      if (e != RN_OK) return e;
+    }
+    if (want_db &&
+        (e = launch(colsum_rows_kernel, dim3(static_cast<unsigned>(cdiv(V, 256))), dim3(256), st,
+                    static_cast<const float*>(zs), L.ldz, static_cast<int>(cr), static_cast<int>(V),
+                    dbs, static_cast<int>(c0 != 0))) != RN_OK)
+      return e;
+  }
+  return launch(loss_sum_kernel, dim3(1), dim3(1024), st, static_cast<const double*>(jt), BT, loss);
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// dl_gemm.h — bf16 matrix product on the MFMA units of gfx950 for the fused linear
+// distillation loss: C[M x N] = A[M x K] * B[N x K]^T, A and B bf16 with K contiguous
+// (row strides lda, ldb in elements), fp32 accumulation.  Every product of the loss is
+// brought to this one shape (the caller transposes what is not K-contiguous):
+//   logits  z[C x V]  = x[C x H] * W[V x H]^T
+//   dx      [C x H]   = dz[C x V] * (W^T)[H x V]^T
+//   dW      [V x H]  += (dz^T)[V x C] * (x^T)[H x C]^T
+//
+// Tiling.  A workgroup of 256 threads (four waves) owns a 128 x 128 tile of C; wave w
+// owns the 64 x 64 quarter (w / 2, w % 2) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+// Lane layout of that instruction (checked on the GPU): lane l holds A[l % 32][8 (l / 32)
+// + e] and B^T[l % 32][8 (l / 32) + e] for e = 0..7, and accumulator r is
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  K advances 64 at a time: the next 128 x 64
+// slices of A and B are loaded from HBM into registers while the current ones are
+// multiplied out of LDS (rows padded to 72 elements against bank conflicts).  Loads go
+// through buffer resources: rows past M (N) and columns past K read zero, so ragged
+// edges need no branches; K must be a multiple of 8.
+//
+// Placement.  Workgroups are dealt to the 8 XCDs round-robin by id.  The ids are mapped
+// so that all row tiles of one column tile of C run on the same XCD at about the same
+// time: the column tile of B (the large operand: the vocabulary head) is then fetched
+// from HBM once into that XCD's L2 and reused by every row tile.
+//
+// Split K (grid.z > 1): workgroup z adds K range z and writes its own fp32 slice of C;
+// a fixed-order sum of the slices follows (deterministic).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+enum : int { EPI_F32 = 0, EPI_F32_ADD = 1, EPI_BF16 = 2 };
+
+struct GemmArgs {
+  const uint16_t* A; int64_t lda;   // [M][lda] bf16 bits
+  const uint16_t* B; int64_t ldb;   // [N][ldb] bf16 bits
+  void* C; int64_t ldc;             // [M][ldc] fp32 or bf16 (EPI_BF16); split K: slices of
+  int64_t split_stride;             //   split_stride elements each
+  const uint16_t* bias;             // [N] bf16 added to every row (EPI_F32 only), or null
+  int M, N, K;
+  int k_per_split;                  // multiple of 64
+  int mt, nt;                       // row / column tiles of C
+};
+
+constexpr int GT = 256;            // threads per workgroup
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int LP = BK + 8;         // LDS row pitch in elements (144 bytes)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float bf16_to_f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// round to nearest even
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {f, 0.0f};
+  return static_cast<uint16_t>(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2)) &
+                               0xffffu);
+}
+
+// Tile (mi, ni) of workgroup `id` (see Placement).  Returns false for the ids that
+// round the grid up to a multiple of 8 column tiles.
+__device__ __forceinline__ bool tile_of(int id, int mt, int nt, int& mi, int& ni) {
+  const int x = id & 7;
+  const int q = id >> 3;
+  mi = q % mt;
+  ni = (q / mt) * 8 + x;
+  return ni < nt;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LP];
+  int mi, ni;
+  if (!tile_of(blockIdx.x, g.mt, g.nt, mi, ni)) return;  // uniform per workgroup
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = mi * BM, n0 = ni * BN;
+  const int kb = blockIdx.z * g.k_per_split;
+  const int ke = min(g.K, kb + g.k_per_split);
+
+  // resources over the workgroup's rows of A and B (rows past M / N read zero)
+  const rsrc_t ra = make_rsrc(g.A + static_cast<int64_t>(m0) * g.lda,
+                              static_cast<uint64_t>(max(0, min(BM, g.M - m0))) * g.lda * 2);
+  const rsrc_t rb = make_rsrc(g.B + static_cast<int64_t>(n0) * g.ldb,
+                              static_cast<uint64_t>(max(0, min(BN, g.N - n0))) * g.ldb * 2);
+
+  // global -> register staging: 128 rows x 64 elements = 1024 chunks of 8 elements
+  // per operand; thread t takes chunks t, t + 256, t + 512, t + 768
+  u32x4 ra_st[4], rb_st[4];
+  auto load_stage = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + GT * i;
+      const int row = c >> 3;
+      const int kc = k0 + (c & 7) * 8;
+      const bool kin = kc < ke;
+      const uint32_t oa = kin ? static_cast<uint32_t>((row * g.lda + kc) * 2) : 0x80000000u;
+      const uint32_t ob = kin ? static_cast<uint32_t>((row * g.ldb + kc) * 2) : 0x80000000u;
+      ra_st[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, oa, 0, 0);
+      rb_st[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0);
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + GT * i;
+      const int row = c >> 3;
+      const int kc = (c & 7) * 8;
+      *reinterpret_cast<u32x4*>(&As[row * LP + kc]) = ra_st[i];
+      *reinterpret_cast<u32x4*>(&Bs[row * LP + kc]) = rb_st[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int arow = wm * 64 + (lane & 31);
+  const int brow = wn * 64 + (lane & 31);
+  const int kl = (lane >> 5) * 8;
+
+  if (kb < ke) load_stage(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    __syncthreads();  // the previous stage's fragments have been read
+    store_stage();
+    __syncthreads();
+    if (k0 + BK < ke) load_stage(k0 + BK);  // next slices in flight during the products
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = *reinterpret_cast<const bf16x8*>(&As[(arow + 32 * i) * LP + kk + kl]);
+        bfr[i] = *reinterpret_cast<const bf16x8*>(&Bs[(brow + 32 * i) * LP + kk + kl]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // epilogue: accumulator r of block (i, j) is C[m][n] with
+  // m = m0 + wm 64 + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, n = n0 + wn 64 + 32 j + lane % 32
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + 32 * j + (lane & 31);
+    if (n >= g.N) continue;
+    float bn = 0.0f;
+    if constexpr (EPI == EPI_F32) {
+      if (g.bias != nullptr && blockIdx.z == 0) bn = bf16_to_f(g.bias[n]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (m >= g.M) continue;
+        const int64_t o = static_cast<int64_t>(m) * g.ldc + n;
+        if constexpr (EPI == EPI_BF16) {
+          static_cast<uint16_t*>(g.C)[o] = f_to_bf16(acc[i][j][r]);
+        } else {
+          float* c = static_cast<float*>(g.C) + blockIdx.z * g.split_stride;
+          if constexpr (EPI == EPI_F32_ADD) c[o] += acc[i][j][r];
+          else c[o] = acc[i][j][r] + bn;
+        }
+      }
+    }
+  }
+}
+
+}  // namespace dl

@@ -19,8 +19,11 @@ def rn():
     return rn
 
 
-def declared_functions():
-    text = open(HEADER).read()
+DISTILL_HEADER = os.path.join(ROOT, "include", "distill.h")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     text = re.sub(r"#[^\n]*", "", text)
@@ -38,8 +41,39 @@ def test_header_declares_the_six_operations():
 
 def test_library_exports_every_declared_symbol(rn):
     lib = ctypes.CDLL(rn.LIB_PATH)
-    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    names = declared_functions() + declared_functions(DISTILL_HEADER)
+    assert "fused_linear_jsd" in names and "fused_linear_jsd_workspace_bytes" in names
+    missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
+
+
+def test_distill_argument_errors(rn):
+    """fused_linear_jsd checks sizes, pointers, strides and the workspace before any HIP
+    call; the workspace query is 0 for unsupported sizes and smaller for a frozen head."""
+    L = rn.lib
+    q = L.fused_linear_jsd_workspace_bytes
+    assert q(4096, 4096, 4096, 128256, 1024, 1, 1, 1) > q(4096, 4096, 4096, 128256, 1024, 1, 0, 0)
+    assert q(4096, 4096, 4096, 128256, 1024, 0, 0, 0) < q(4096, 4096, 4096, 128256, 1024, 1, 0, 0)
+    assert q(4096, 4100, 4096, 128256, 1024, 1, 1, 1) == 0      # H not a multiple of 8
+    assert q(-1, 64, 64, 100, 16, 1, 1, 1) == 0 and q(16, 64, 64, 0, 16, 1, 1, 1) == 0
+    f = L.fused_linear_jsd
+    A = ctypes.c_void_p(4096)
+    need = q(16, 64, 64, 100, 8, 1, 1, 0)
+    ok = dict(xs=A, ldxs=64, ws=A, bs=None, xt=A, ldxt=64, wt=A, bt=None, BT=16, H=64, Ht=64,
+              V=100, beta=0.5, tau=1.0, chunk=8, loss=A, dx=A, lddx=64, dw=ctypes.c_void_p(8192),
+              db=None, ws_buf=ctypes.c_void_p(1 << 20), ws_bytes=need, stream=None)
+
+    def call(**over):
+        a = {**ok, **over}
+        return f(*a.values())
+    assert call(H=60) == E_SHAPE
+    assert call(beta=1.5) == E_SHAPE and call(tau=0.0) == E_SHAPE
+    assert call(loss=None) == E_NULL and call(xs=None) == E_NULL
+    assert call(db=A) == E_NULL                                # db without a bias
+    assert call(ws_bytes=need - 1) == E_WS
+    assert call(ws_buf=ctypes.c_void_p((1 << 20) + 16)) == E_WS   # not 256-byte aligned
+    assert call(ldxs=60) == E_STRIDE and call(ldxs=68) == E_STRIDE
+    assert call(xs=ctypes.c_void_p(4104)) == E_STRIDE        # not 16-byte aligned
 
 
 RN_OK, E_NULL, E_SHAPE, E_DTYPE, E_STRIDE, E_WS, E_HIP, E_ALIAS, E_INT, E_SCRATCH = (

@@ -140,3 +140,48 @@ def small(op: str, M: int, N: int, io: str = "bf16", wt: str | None = None, *,
 def as_f64(t: torch.Tensor):
     """Exact fp64 numpy copy of a stored tensor (for the oracle)."""
     return t.detach().to("cpu").double().numpy()
+
+
+# ---- fused linear JSD distillation loss ---------------------------------------------
+# "perf(distillation): skip dW/dB calculation when parameters are frozen", Details:
+# B*T = 4096 tokens, H = 4096, V = 128256 (and 151936), chunks of 1024 tokens, bf16.  The
+# page gives no value distributions: activations are standard normal and head weights
+# normal with standard deviation 1/sqrt(H) (logits of order one), biases 0.1 * normal.
+
+@dataclass(frozen=True)
+class DistillWorkload:
+    """One synthetic distillation problem: sizes, loss parameters and which parts exist."""
+    name: str
+    BT: int
+    H: int
+    Ht: int
+    V: int
+    chunk: int = 1024
+    beta: float = 0.5
+    temperature: float = 1.0
+    bias: bool = False
+    seed: int = 42
+
+
+DISTILL_4096x4096_V128256 = DistillWorkload("distill_jsd_4096x4096_v128256", 4096, 4096, 4096,
+                                            128256)
+DISTILL_4096x4096_V151936 = DistillWorkload("distill_jsd_4096x4096_v151936", 4096, 4096, 4096,
+                                            151936)
+DISTILL_CONFIGS = [DISTILL_4096x4096_V128256, DISTILL_4096x4096_V151936]
+
+
+def generate_distill(wl: DistillWorkload) -> dict:
+    """Draw the distillation inputs on the CPU, in the order xs, ws, bs, xt, wt, bt
+    (biases only when wl.bias), float32 draws cast to bf16."""
+    g = torch.Generator().manual_seed(wl.seed)
+    bf = torch.bfloat16
+
+    def n(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=g, dtype=torch.float32) * scale).to(bf)
+
+    out = {"xs": n(wl.BT, wl.H), "ws": n(wl.V, wl.H, scale=wl.H ** -0.5)}
+    out["bs"] = n(wl.V, scale=0.1) if wl.bias else None
+    out["xt"] = n(wl.BT, wl.Ht)
+    out["wt"] = n(wl.V, wl.Ht, scale=wl.Ht ** -0.5)
+    out["bt"] = n(wl.V, scale=0.1) if wl.bias else None
+    return out
