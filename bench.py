@@ -394,6 +394,65 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def distill_flops(wl, dx=True, dw=True) -> float:
+    """Products of the fused linear JSD loss: student and teacher logits (2 B T V H
+    each), dx = dz W and dW = dz^T x (2 B T V H each, when requested)."""
+    one = 2.0 * wl.BT * wl.V * wl.H
+    return one * (2 + int(dx) + int(dw))
+
+
+def measure_distill(wl, rounds, torch, seed=1):
+    """The distillation loss at one size: providers trainable (dx and dW), frozen (dx
+    only: the student head frozen, [distill] Summary) and an identical trainable A/A
+    duplicate, each call timed with HIP events, shuffled per round; medians in ms."""
+    from normalization_row_wise_amd import distill
+    t = workloads.generate_distill(wl)
+    d = {k: (v.to("cuda:0") if v is not None else None) for k, v in t.items()}
+    need = distill.workspace_bytes(wl.BT, wl.H, wl.Ht, wl.V, wl.chunk, True, True, True)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda:0")
+    dx = torch.empty(wl.BT, wl.H, dtype=torch.bfloat16, device="cuda:0")
+    dw = torch.empty(wl.V, wl.H, dtype=torch.float32, device="cuda:0")
+
+    def call(p):
+        distill.fused_linear_jsd(d["xs"], d["ws"], d["xt"], d["wt"], d["bs"], d["bt"], wl.beta,
+                                 wl.temperature, wl.chunk, dx=dx,
+                                 dw=None if p == "frozen" else dw, db=None, workspace=ws)
+
+    provs = ("trainable", "frozen", "trainable_aa")
+    for p in provs:
+        call(p)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    rng = random.Random(seed)
+    per = {p: [] for p in provs}
+    for _ in range(rounds):
+        order = list(provs)
+        rng.shuffle(order)
+        for p in order:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(st)
+            call(p)
+            e1.record(st)
+            torch.cuda.synchronize()
+            per[p].append(e0.elapsed_time(e1))
+    med = {p: median(v) for p, v in per.items()}
+    del d, ws, dx, dw
+    torch.cuda.empty_cache()
+    ft, ff = distill_flops(wl, True, True), distill_flops(wl, True, False)
+    return {"BT": wl.BT, "H": wl.H, "V": wl.V, "chunk": wl.chunk,
+            "ms_per_call": {p: round(v, 3) for p, v in med.items()},
+            "aa_delta_pct": round(100 * (med["trainable_aa"] / med["trainable"] - 1), 2),
+            "frozen_saving_pct": round(100 * (1 - med["frozen"] / med["trainable"]), 1),
+            "tflops": {"trainable": round(ft / (med["trainable"] * 1e-3) / 1e12, 1),
+                       "frozen": round(ff / (med["frozen"] * 1e-3) / 1e12, 1)},
+            "pct_of_bf16_mfma_peak": round(100 * ft / (med["trainable"] * 1e-3) / 1e12
+                                           / MFMA_BF16_PEAK_TFLOPS, 2)}
+
+
 # Configurations timed beside the headline, reported as extra keys of the same line.
 EXTRA = ("layernorm_2048x4096_bf16", "fused_add_rmsnorm_2048x8192_bf16")
 
@@ -496,6 +555,11 @@ def main():
             del e["sets"], e
             torch.cuda.empty_cache()
 
+    distill_lines = {}
+    if not args.no_extra:
+        for dwl in workloads.DISTILL_CONFIGS:
+            distill_lines[dwl.name] = measure_distill(dwl, max(3, args.rounds // 2), torch)
+
     med = m["us_per_step"]
     line = {
         "metric": "achieved HBM GB/s (% of peak) & µs/call, bf16 norm fwd+bwd at M×N",
@@ -533,6 +597,7 @@ def main():
                      "avg_launch_us": round(k1_us, 3),
                      "stream_ceiling": ceiling},
         "extra_configs": extra,
+        "distill_jsd": distill_lines,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
