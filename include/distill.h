@@ -19,11 +19,18 @@
  * teacher is a fixed target: gradients are for the student's input, weight and bias.
  *
  * Arithmetic: the products on the MFMA units in bf16 with fp32 accumulation; the
- * per-token softmax, divergence and logit gradient in fp32 with fp64 row sums; the logit
- * gradient is rounded to bf16 before the two gradient products (dx, dW), whose
- * accumulation is fp32; dx is stored in bf16, dW and db in fp32, the loss in fp32.
- * Every reduction has a fixed order: results are bitwise reproducible, and the loss and
- * dx do not depend on which parameter gradients are requested.
+ * per-token softmax, divergence and logit gradient in fp32 with fp64 row sums, e^x and
+ * ln x per vocabulary entry through the hardware's base-2 exponential and logarithm
+ * (relative error about 1e-6 at the magnitudes that carry weight); the logit gradient is
+ * rounded to bf16 before the two gradient products (dx, dW), whose accumulation is fp32;
+ * dx is stored in bf16, dW and db in fp32, the loss in fp32.  Every reduction has a
+ * fixed order: results are bitwise reproducible, and the loss and dx do not depend on
+ * which parameter gradients are requested.
+ *
+ * Schedule: per chunk, the two logits products, the per-token statistics, the logit
+ * gradient and the dx product; dW is one product over all tokens after the last chunk
+ * (the bf16 transposed logit gradient of every token is kept for it), so the chunking
+ * bounds the fp32 logits, 2 x chunk x V x 4 bytes, not the dW input.
  *
  * Conventions: all pointers are DEVICE pointers owned by the caller; the call only
  * enqueues kernels on `stream` (no allocation, no synchronisation).  Matrices are
@@ -43,10 +50,12 @@ extern "C" {
 #endif
 
 /* Workspace bytes of fused_linear_jsd for these sizes and requested gradients
- * (want_* = 0 / 1): two fp32 logit blocks of chunk x V, per-token divergences, and for
- * dx the bf16 logit gradient, the transposed student weight and split partial sums, for
- * dw the transposed gradient and input chunk.  A frozen head (want_dw = 0) needs none of
- * the dW buffers ([distill], Summary).  0 for invalid sizes. */
+ * (want_* = 0 / 1): two fp32 logit blocks of chunk x V, per-token statistics, and for
+ * dx the bf16 logit gradient of a chunk, the transposed student weight and split partial
+ * sums; for dw the bf16 transposed logit gradient of all tokens (V x BT) and the
+ * transposed student input (H x BT); for db column sums per 64 tokens of a chunk.  A
+ * frozen head (want_dw = 0) needs none of the dW buffers ([distill], Summary).  0 for
+ * invalid sizes (with want_dw, BT rounded up to 8 must not exceed 2^22). */
 size_t fused_linear_jsd_workspace_bytes(int64_t BT, int64_t H, int64_t Ht, int64_t V,
                                         int64_t chunk, int want_dx, int want_dw, int want_db);
 

@@ -1,10 +1,20 @@
 // dl_abi.hip — the C ABI of the fused linear JSD distillation loss (include/distill.h):
 // argument checks, workspace layout and the chunk loop ([distill], Summary and Details:
 // tokens in chunks, the student head's weight gradient skipped when frozen).
+//
+// Per call: W_s^T once (dx), x_s^T once (dW); per chunk of C tokens: the two logits
+// products, the per-token statistics, the logit gradient (bf16 rows for dx, bf16 columns
+// of dz^T for dW, fp32 column sums for db), the dx product; after the last chunk one dW
+// product over all tokens.  The fp32 logits (2 C V) are the chunked memory; dz^T is kept
+// for every token (2 bytes per token and vocabulary entry) so that dW is one product with
+// K = tokens instead of an fp32 read-modify-write of [V, H] per chunk.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "../../include/distill.h"
 #include "dl_kernels.h"
@@ -16,25 +26,27 @@ namespace {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Split of the dx product's K (= V) so that it has about 1024 workgroups.
+// Split of the dx product's K (= V) so that it has about two workgroups per CU (one
+// fits at a time: the GEMM takes 144 KiB of LDS).
 inline int dx_splits(int64_t chunk, int64_t H) {
   const int64_t tiles = cdiv(chunk, BM) * cdiv(H, BN);
-  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, 1024 / std::max<int64_t>(1, tiles))));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, 512 / std::max<int64_t>(1, tiles))));
 }
 
 // Byte offsets of the workspace parts (each 256-byte aligned); total in `end`.
 struct Layout {
-  size_t zs, zt, gb, wst, dxp, gbt, xst, jt, end;
-  int64_t ldz, vpad, ldk;
+  size_t zs, zt, stats, gb, wst, dxp, gbt, xst, dbp, jt, end;
+  int64_t C, ldz, vpad, ldt;
   int splits;
 };
 
-Layout layout(int64_t BT, int64_t H, int64_t V, int64_t chunk, bool dx, bool dw) {
+Layout layout(int64_t BT, int64_t H, int64_t V, int64_t chunk, bool dx, bool dw, bool db) {
   Layout L{};
   const int64_t c = std::min(chunk, std::max<int64_t>(BT, 1));
+  L.C = c;
   L.ldz = rup(V, 4);
   L.vpad = rup(V, 8);
-  L.ldk = rup(c, 8);
+  L.ldt = rup(std::max<int64_t>(BT, 1), 8);
   L.splits = dx ? dx_splits(c, H) : 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -44,23 +56,26 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int64_t chunk, bool dx, bool dw)
   };
   L.zs = take(static_cast<size_t>(c) * L.ldz * 4);
   L.zt = take(static_cast<size_t>(c) * L.ldz * 4);
+  L.stats = take(static_cast<size_t>(c) * 16);
   L.gb = dx ? take(static_cast<size_t>(c) * L.vpad * 2) : 0;
   L.wst = dx ? take(static_cast<size_t>(H) * L.vpad * 2) : 0;
   L.dxp = dx ? take(static_cast<size_t>(L.splits) * c * H * 4) : 0;
-  L.gbt = dw ? take(static_cast<size_t>(V) * L.ldk * 2) : 0;
-  L.xst = dw ? take(static_cast<size_t>(H) * L.ldk * 2) : 0;
+  L.gbt = dw ? take(static_cast<size_t>(V) * L.ldt * 2) : 0;
+  L.xst = dw ? take(static_cast<size_t>(H) * L.ldt * 2) : 0;
+  L.dbp = db ? take(static_cast<size_t>(cdiv(c, GR_ROWS)) * V * 4) : 0;
   L.jt = take(static_cast<size_t>(std::max<int64_t>(BT, 1)) * 8);
   L.end = o;
   return L;
 }
 
-bool valid_sizes(int64_t BT, int64_t H, int64_t Ht, int64_t V, int64_t chunk) {
+bool valid_sizes(int64_t BT, int64_t H, int64_t Ht, int64_t V, int64_t chunk, bool dw) {
   if (BT < 0 || H < 8 || Ht < 8 || V < 1 || chunk < 1) return false;
   if (H % 8 || Ht % 8) return false;
-  // in-tile byte offsets of the products stay below 2^31: 128 rows of at most 2^22
-  // elements (V padded, H, the input strides)
+  // in-tile byte offsets of the products stay below 2^31: 256 rows of at most 2^22
+  // elements (V padded, H, the input strides, the tokens padded for dW)
   if (V > (int64_t(1) << 22) - 8 || H > (int64_t(1) << 20) || Ht > (int64_t(1) << 20)) return false;
   if (BT > (int64_t(1) << 31)) return false;
+  if (dw && rup(BT, 8) > (int64_t(1) << 22)) return false;
   // every buffer addressed with 32-bit byte offsets: the weights, a chunk's logits
   if (V * std::max(H, Ht) * 2 >= (int64_t(1) << 32)) return false;
   if (std::min(chunk, std::max<int64_t>(BT, 1)) * rup(V, 4) * 4 >= (int64_t(1) << 32)) return false;
@@ -71,19 +86,35 @@ bool valid_sizes(int64_t BT, int64_t H, int64_t Ht, int64_t V, int64_t chunk) {
 inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <typename K, typename... Args>
-int launch(K k, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+int launch(K k, dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args) {
   void* a[] = {&args...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, a, 0, s) == hipSuccess
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, a, shmem, s) == hipSuccess
              ? RN_OK
              : RN_ERR_HIP;
 }
 
-// C[M x N] (+)= A[M x K] B[N x K]^T with `splits` K ranges written to slices of C.
-template <int EPI>
-int gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C, int64_t ldc,
+// The GEMM's two LDS stages exceed the default dynamic LDS limit; raised once per device.
+bool allow_gemm_lds() {
+  static std::mutex mu;
+  static std::set<int> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> g(mu);
+  if (done.count(dev)) return true;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nt_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(kGemmLds)) != hipSuccess)
+    return false;
+  done.insert(dev);
+  return true;
+}
+
+// C[M x N] = A[M x K] B[N x K]^T (+ bias) with `splits` K ranges written to slices of C.
+int gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C, int64_t ldc,
          int64_t split_stride, const uint16_t* bias, int64_t M, int64_t N, int64_t K, int splits,
          hipStream_t s) {
   if (M == 0 || N == 0) return RN_OK;
+  if (!allow_gemm_lds()) return RN_ERR_HIP;
   GemmArgs g{};
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.split_stride = split_stride; g.bias = bias;
@@ -92,7 +123,16 @@ int gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C
   g.mt = static_cast<int>(cdiv(M, BM));
   g.nt = static_cast<int>(cdiv(N, BN));
   const dim3 grid(static_cast<unsigned>(8 * cdiv(g.nt, 8) * g.mt), 1, static_cast<unsigned>(splits));
-  return launch(gemm_nt_kernel<EPI>, grid, dim3(GT), s, g);
+  return launch(gemm_nt_kernel, grid, dim3(GT), kGemmLds, s, g);
+}
+
+// out[c][r] = in[r][c] for R x Cc, zeros for r in [R, Rpad)
+int transpose(const uint16_t* in, int64_t ldi, int64_t R, int64_t Cc, uint16_t* out, int64_t ldo,
+              int64_t Rpad, hipStream_t s) {
+  return launch(transpose_bf16_kernel,
+                dim3(static_cast<unsigned>(cdiv(Cc, 64)), static_cast<unsigned>(cdiv(Rpad, 64))),
+                dim3(256), 0, s, in, ldi, static_cast<int>(R), static_cast<int>(Cc), out, ldo,
+                static_cast<int>(Rpad));
 }
 
 }  // namespace
@@ -101,9 +141,8 @@ extern "C" {
 
 size_t fused_linear_jsd_workspace_bytes(int64_t BT, int64_t H, int64_t Ht, int64_t V,
                                         int64_t chunk, int want_dx, int want_dw, int want_db) {
-  (void)want_db;
-  if (!valid_sizes(BT, H, Ht, V, chunk)) return 0;
-  return layout(BT, H, V, chunk, want_dx != 0, want_dw != 0).end;
+  if (!valid_sizes(BT, H, Ht, V, chunk, want_dw != 0)) return 0;
+  return layout(BT, H, V, chunk, want_dx != 0, want_dw != 0, want_db != 0).end;
 }
 
 int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const void* bs,
@@ -111,12 +150,12 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
                      int64_t H, int64_t Ht, int64_t V, float beta, float temperature,
                      int64_t chunk, float* loss, void* dxs, int64_t lddx, float* dws, float* dbs,
                      void* ws, size_t ws_bytes, hipStream_t st) {
-  if (!valid_sizes(BT, H, Ht, V, chunk)) return RN_ERR_SHAPE;
+  const bool want_dx = dxs != nullptr, want_dw = dws != nullptr, want_db = dbs != nullptr;
+  if (!valid_sizes(BT, H, Ht, V, chunk, want_dw)) return RN_ERR_SHAPE;
   if (!(beta >= 0.0f && beta <= 1.0f) || !(temperature > 0.0f)) return RN_ERR_SHAPE;
   if (loss == nullptr || ws == nullptr) return RN_ERR_NULL;
   if (dbs != nullptr && bs == nullptr) return RN_ERR_NULL;
-  const bool want_dx = dxs != nullptr, want_dw = dws != nullptr, want_db = dbs != nullptr;
-  const Layout L = layout(BT, H, V, chunk, want_dx, want_dw);
+  const Layout L = layout(BT, H, V, chunk, want_dx, want_dw, want_db);
   if (ws_bytes < L.end || (reinterpret_cast<uintptr_t>(ws) & 255u)) return RN_ERR_WORKSPACE;
   if (BT > 0) {
     if (xs == nullptr || ws_weight == nullptr || xt == nullptr || wt == nullptr) return RN_ERR_NULL;
@@ -131,11 +170,13 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
   char* base = static_cast<char*>(ws);
   float* zs = reinterpret_cast<float*>(base + L.zs);
   float* zt = reinterpret_cast<float*>(base + L.zt);
+  float* stats = reinterpret_cast<float*>(base + L.stats);
   uint16_t* gb = want_dx ? reinterpret_cast<uint16_t*>(base + L.gb) : nullptr;
   uint16_t* wst = want_dx ? reinterpret_cast<uint16_t*>(base + L.wst) : nullptr;
   float* dxp = want_dx ? reinterpret_cast<float*>(base + L.dxp) : nullptr;
   uint16_t* gbt = want_dw ? reinterpret_cast<uint16_t*>(base + L.gbt) : nullptr;
   uint16_t* xst = want_dw ? reinterpret_cast<uint16_t*>(base + L.xst) : nullptr;
+  float* dbp = want_db ? reinterpret_cast<float*>(base + L.dbp) : nullptr;
   double* jt = reinterpret_cast<double*>(base + L.jt);
   const auto* Xs = static_cast<const uint16_t*>(xs);
   const auto* Ws = static_cast<const uint16_t*>(ws_weight);
@@ -147,81 +188,79 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
   int e = RN_OK;
 
   if (BT == 0) {  // empty batch: loss 0, gradients 0
-    if ((e = launch(loss_sum_kernel, dim3(1), dim3(1024), st, static_cast<const double*>(jt),
+    if ((e = launch(loss_sum_kernel, dim3(1), dim3(1024), 0, st, static_cast<const double*>(jt),
                     int64_t(0), loss)) != RN_OK)
       return e;
     if (want_dw && (e = launch(fill_zero_kernel, dim3(static_cast<unsigned>(cdiv(V * H, 256))),
-                               dim3(256), st, dws, V * H)) != RN_OK)
+                               dim3(256), 0, st, dws, V * H)) != RN_OK)
       return e;
     if (want_db && (e = launch(fill_zero_kernel, dim3(static_cast<unsigned>(cdiv(V, 256))), dim3(256),
-                               st, dbs, V)) != RN_OK)
+                               0, st, dbs, V)) != RN_OK)
       return e;
     return RN_OK;
   }
 
   // W_s^T [H][vpad] (zero columns past V): the K-contiguous operand of the dx product
-  if (want_dx &&
-      (e = launch(transpose_bf16_kernel<uint16_t>,
-                  dim3(static_cast<unsigned>(cdiv(H, 64)), static_cast<unsigned>(cdiv(L.vpad, 64))),
-                  dim3(256), st, Ws, H, static_cast<int>(V), static_cast<int>(H), wst, L.vpad,
-                  static_cast<int>(L.vpad))) != RN_OK)
-    return e;
+  if (want_dx && (e = transpose(Ws, H, V, H, wst, L.vpad, L.vpad, st)) != RN_OK) return e;
+  // x_s^T [H][ldt] (zero columns past BT): the second operand of the dW product
+  if (want_dw && (e = transpose(Xs, ldxs, BT, H, xst, L.ldt, L.ldt, st)) != RN_OK) return e;
 
-  const int64_t C = std::min(chunk, BT);
-  for (int64_t c0 = 0; c0 < BT; c0 += C) {
-    const int64_t cr = std::min(C, BT - c0);
+  const bool want_grad = want_dx || want_dw || want_db;
+  const float inv_tau = 1.0f / temperature;
+  for (int64_t c0 = 0; c0 < BT; c0 += L.C) {
+    const int64_t cr = std::min(L.C, BT - c0);
+    const bool last = c0 + cr == BT;
     // logits of the chunk (fp32; the bias added in the epilogue)
-    if ((e = gemm<EPI_F32>(Xs + c0 * ldxs, ldxs, Ws, H, zs, L.ldz, 0, Bs, cr, V, H, 1, st)) != RN_OK)
+    if ((e = gemm(Xs + c0 * ldxs, ldxs, Ws, H, zs, L.ldz, 0, Bs, cr, V, H, 1, st)) != RN_OK)
       return e;
-    if ((e = gemm<EPI_F32>(Xt + c0 * ldxt, ldxt, Wt, Ht, zt, L.ldz, 0, Bt, cr, V, Ht, 1, st)) !=
-        RN_OK)
+    if ((e = gemm(Xt + c0 * ldxt, ldxt, Wt, Ht, zt, L.ldz, 0, Bt, cr, V, Ht, 1, st)) != RN_OK)
       return e;
-    // divergence per token and, if any gradient is wanted, dL/dz (bf16 for dx, fp32 in
-    // place of the student logits for dW and db)
-    JsdArgs j{};
-    j.zs = zs; j.zt = zt; j.ldz = L.ldz; j.gb = gb; j.ldg = L.vpad; j.jtok = jt + c0;
-    j.rows = static_cast<int>(cr); j.V = static_cast<int>(V); j.vpad = static_cast<int>(L.vpad);
-    j.beta = beta; j.inv_tau = 1.0f / temperature;
-    j.grad_scale = static_cast<float>(1.0 / (static_cast<double>(temperature) * static_cast<double>(BT)));
-    j.want_grad = want_dx || want_dw || want_db;
-    j.write_f32 = want_dw || want_db;
-    if ((e = launch(jsd_rows_kernel, dim3(static_cast<unsigned>(cr)), dim3(JT), st, j)) != RN_OK)
+    // per token: log-sum-exps, J, A
+    StatArgs sa{};
+    sa.zs = zs; sa.zt = zt; sa.ldz = L.ldz; sa.stats = stats; sa.jtok = jt + c0;
+    sa.rows = static_cast<int>(cr); sa.V = static_cast<int>(V);
+    sa.beta = beta; sa.inv_tau = inv_tau;
+    if ((e = launch(jsd_stats_kernel, dim3(static_cast<unsigned>(cr)), dim3(JT), 0, st, sa)) != RN_OK)
+      return e;
+    if (!want_grad) continue;
+    // dL/dz: bf16 rows (dx), bf16 columns of dz^T (dW; the last chunk also zeroes the
+    // token padding), fp32 column sums per 64 rows (db)
+    GradArgs ga{};
+    ga.zs = zs; ga.zt = zt; ga.ldz = L.ldz; ga.stats = stats;
+    ga.rows = static_cast<int>(cr); ga.V = static_cast<int>(V);
+    ga.beta = beta; ga.inv_tau = inv_tau;
+    ga.grad_scale = static_cast<float>(1.0 / (static_cast<double>(temperature) * static_cast<double>(BT)));
+    ga.gb = gb; ga.ldg = L.vpad; ga.vpad = static_cast<int>(L.vpad);
+    ga.gbt = gbt; ga.ldt = L.ldt; ga.tok0 = c0;
+    ga.tok_rows = static_cast<int>(last ? L.ldt - c0 : cr);
+    ga.dbp = dbp;
+    const int64_t grid_rows = want_dw ? std::max<int64_t>(cr, ga.tok_rows) : cr;
+    if ((e = launch(jsd_grad_kernel,
+                    dim3(static_cast<unsigned>(cdiv(L.vpad, GR_COLS)),
+                         static_cast<unsigned>(cdiv(grid_rows, GR_ROWS))),
+                    dim3(GR_T), 0, st, ga)) != RN_OK)
       return e;
     if (want_dx) {
       // dx[c0 .. c0 + cr) = dz W_s: K = V in `splits` ranges, then their fixed-order sum
-      if ((e = gemm<EPI_F32>(gb, L.vpad, wst, L.vpad, dxp, H, cr * H, nullptr, cr, H, L.vpad,
-                             L.splits, st)) != RN_OK)
+      if ((e = gemm(gb, L.vpad, wst, L.vpad, dxp, H, cr * H, nullptr, cr, H, L.vpad, L.splits,
+                    st)) != RN_OK)
         return e;
       if ((e = launch(split_sum_bf16_kernel, dim3(static_cast<unsigned>(cdiv(cr * H, 256))),
-                      dim3(256), st, static_cast<const float*>(dxp), cr * H, L.splits,
+                      dim3(256), 0, st, static_cast<const float*>(dxp), cr * H, L.splits,
                       static_cast<int>(cr), static_cast<int>(H), H, Dx + c0 * lddx, lddx)) != RN_OK)
         return e;
     }
-    if (want_dw) {
-      // dW (+)= dz^T x_s: both operands transposed to K (the chunk's tokens) contiguous,
-      // K padded with zeros to a multiple of 8.  Skipped entirely for a frozen weight.
-      const int ck = static_cast<int>(rup(cr, 8));
-      if ((e = launch(transpose_bf16_kernel<float>,
-                      dim3(static_cast<unsigned>(cdiv(V, 64)), static_cast<unsigned>(cdiv(ck, 64))),
-                      dim3(256), st, static_cast<const float*>(zs), L.ldz, static_cast<int>(cr),
-                      static_cast<int>(V), gbt, L.ldk, ck)) != RN_OK)
-        return e;
-      if ((e = launch(transpose_bf16_kernel<uint16_t>,
-                      dim3(static_cast<unsigned>(cdiv(H, 64)), static_cast<unsigned>(cdiv(ck, 64))),
-                      dim3(256), st, Xs + c0 * ldxs, ldxs, static_cast<int>(cr), static_cast<int>(H),
-                      xst, L.ldk, ck)) != RN_OK)
-        return e;
-      e = c0 == 0 ? gemm<EPI_F32>(gbt, L.ldk, xst, L.ldk, dws, H, 0, nullptr, V, H, ck, 1, st)
-                  : gemm<EPI_F32_ADD>(gbt, L.ldk, xst, L.ldk, dws, H, 0, nullptr, V, H, ck, 1, st);
-      if (e != RN_OK) return e;
-    }
     if (want_db &&
-        (e = launch(colsum_rows_kernel, dim3(static_cast<unsigned>(cdiv(V, 256))), dim3(256), st,
-                    static_cast<const float*>(zs), L.ldz, static_cast<int>(cr), static_cast<int>(V),
-                    dbs, static_cast<int>(c0 != 0))) != RN_OK)
+        (e = launch(colsum_rows_kernel, dim3(static_cast<unsigned>(cdiv(V, 256))), dim3(256), 0, st,
+                    static_cast<const float*>(dbp), V, static_cast<int>(cdiv(cr, GR_ROWS)),
+                    static_cast<int>(V), dbs, static_cast<int>(c0 != 0))) != RN_OK)
       return e;
   }
-  return launch(loss_sum_kernel, dim3(1), dim3(1024), st, static_cast<const double*>(jt), BT, loss);
+  // dW = dz^T x_s over all tokens (K padded with zeros to a multiple of 8).  Skipped
+  // entirely, with its buffers, for a frozen weight.
+  if (want_dw && (e = gemm(gbt, L.ldt, xst, L.ldt, dws, H, 0, nullptr, V, H, L.ldt, 1, st)) != RN_OK)
+    return e;
+  return launch(loss_sum_kernel, dim3(1), dim3(1024), 0, st, static_cast<const double*>(jt), BT, loss);
 }
 
 }  // extern "C"

@@ -1,25 +1,32 @@
 // dl_gemm.h — bf16 matrix product on the MFMA units of gfx950 for the fused linear
-// distillation loss: C[M x N] = A[M x K] * B[N x K]^T, A and B bf16 with K contiguous
-// (row strides lda, ldb in elements), fp32 accumulation.  Every product of the loss is
-// brought to this one shape (the caller transposes what is not K-contiguous):
+// distillation loss: C[M x N] = A[M x K] * B[N x K]^T (+ bias[N]), A and B bf16 with K
+// contiguous (row strides lda, ldb in elements), fp32 accumulation and fp32 C.  Every
+// product of the loss is brought to this one shape (the caller transposes what is not
+// K-contiguous):
 //   logits  z[C x V]  = x[C x H] * W[V x H]^T
 //   dx      [C x H]   = dz[C x V] * (W^T)[H x V]^T
-//   dW      [V x H]  += (dz^T)[V x C] * (x^T)[H x C]^T
+//   dW      [V x H]   = (dz^T)[V x T] * (x^T)[H x T]^T      (T: all tokens of the call)
 //
-// Tiling.  A workgroup of 256 threads (four waves) owns a 128 x 128 tile of C; wave w
-// owns the 64 x 64 quarter (w / 2, w % 2) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+// Tiling.  A workgroup of 512 threads (eight waves in a 2 x 4 grid) owns a 256 x 256
+// tile of C; each wave owns 128 x 64 of it as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
 // Lane layout of that instruction (checked on the GPU): lane l holds A[l % 32][8 (l / 32)
 // + e] and B^T[l % 32][8 (l / 32) + e] for e = 0..7, and accumulator r is
-// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  K advances 64 at a time: the next 128 x 64
-// slices of A and B are loaded from HBM into registers while the current ones are
-// multiplied out of LDS (rows padded to 72 elements against bank conflicts).  Loads go
-// through buffer resources: rows past M (N) and columns past K read zero, so ragged
-// edges need no branches; K must be a multiple of 8.
+// C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].  K advances 64 at a time through two LDS
+// stages (rows padded to 72 elements, which keeps the 16-byte fragment reads free of
+// bank conflicts): the next 256 x 64 slices of A and B are loaded from HBM into
+// registers before the products of the current stage and written to the other stage
+// after them, so one barrier per slice suffices.  Per CU and slice the LDS serves 192 KiB
+// of fragment reads and 64 KiB of stores against 2 x 32 MFMAs per SIMD; the 128 x 128
+// tile of four waves needed a third more LDS traffic per product and was 15-20 % slower
+// on these shapes.  The two stages (144 KiB) leave room for one workgroup per CU.
+// Loads go through buffer resources: rows past M (N) and columns past K read zero, so
+// ragged edges need no branches; K must be a multiple of 8, and 256 rows of A or B must
+// span less than 2^31 bytes (lda, ldb <= 2^22).
 //
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin by id.  The ids are mapped
 // so that all row tiles of one column tile of C run on the same XCD at about the same
-// time: the column tile of B (the large operand: the vocabulary head) is then fetched
-// from HBM once into that XCD's L2 and reused by every row tile.
+// time: the column tile of B is then fetched from HBM once into that XCD's L2 and reused
+// by every row tile.
 //
 // Split K (grid.z > 1): workgroup z adds K range z and writes its own fp32 slice of C;
 // a fixed-order sum of the slices follows (deterministic).
@@ -34,26 +41,30 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 
-enum : int { EPI_F32 = 0, EPI_F32_ADD = 1, EPI_BF16 = 2 };
-
 struct GemmArgs {
   const uint16_t* A; int64_t lda;   // [M][lda] bf16 bits
   const uint16_t* B; int64_t ldb;   // [N][ldb] bf16 bits
-  void* C; int64_t ldc;             // [M][ldc] fp32 or bf16 (EPI_BF16); split K: slices of
-  int64_t split_stride;             //   split_stride elements each
-  const uint16_t* bias;             // [N] bf16 added to every row (EPI_F32 only), or null
+  float* C; int64_t ldc;            // [M][ldc]; split K: slices of split_stride elements
+  int64_t split_stride;
+  const uint16_t* bias;             // [N] bf16 added to every row (slice 0 only), or null
   int M, N, K;
   int k_per_split;                  // multiple of 64
   int mt, nt;                       // row / column tiles of C
 };
 
-constexpr int GT = 256;            // threads per workgroup
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int GT = 512;            // threads per workgroup
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LP = BK + 8;         // LDS row pitch in elements (144 bytes)
+constexpr int kStage = (BM + BN) * LP;                          // elements per LDS stage
+constexpr size_t kGemmLds = static_cast<size_t>(2) * kStage * 2;  // 147456 bytes, dynamic
 
+// The size is the same in every lane but may be computed with vector instructions (a
+// clamp becomes v_med3); readfirstlane keeps the resource in scalar registers, without
+// which every load through it is compiled as a loop over the lanes' distinct resources.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(n)),
                                            0x00020000);
 }
 
@@ -79,16 +90,15 @@ __device__ __forceinline__ bool tile_of(int id, int mt, int nt, int& mi, int& ni
   return ni < nt;
 }
 
-template <int EPI>
 __global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LP];
+  extern __shared__ u32x4 gemm_lds[];
+  uint16_t* const stage0 = reinterpret_cast<uint16_t*>(gemm_lds);
   int mi, ni;
   if (!tile_of(blockIdx.x, g.mt, g.nt, mi, ni)) return;  // uniform per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int m0 = mi * BM, n0 = ni * BN;
   const int kb = blockIdx.z * g.k_per_split;
   const int ke = min(g.K, kb + g.k_per_split);
@@ -99,10 +109,10 @@ __global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmArgs g) {
   const rsrc_t rb = make_rsrc(g.B + static_cast<int64_t>(n0) * g.ldb,
                               static_cast<uint64_t>(max(0, min(BN, g.N - n0))) * g.ldb * 2);
 
-  // global -> register staging: 128 rows x 64 elements = 1024 chunks of 8 elements
-  // per operand; thread t takes chunks t, t + 256, t + 512, t + 768
+  // global -> register staging: 256 rows x 64 elements = 2048 chunks of 8 elements per
+  // operand; thread t takes chunks t + 512 i, i = 0..3
   u32x4 ra_st[4], rb_st[4];
-  auto load_stage = [&](int k0) {
+  auto load_slice = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + GT * i;
@@ -115,7 +125,8 @@ __global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmArgs g) {
       rb_st[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, ob, 0, 0);
     }
   };
-  auto store_stage = [&]() {
+  auto store_slice = [&](uint16_t* As) {
+    uint16_t* Bs = As + BM * LP;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + GT * i;
@@ -126,62 +137,65 @@ __global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int arow = wm * 64 + (lane & 31);
+  const int arow = wm * 128 + (lane & 31);
   const int brow = wn * 64 + (lane & 31);
   const int kl = (lane >> 5) * 8;
-
-  if (kb < ke) load_stage(kb);
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    __syncthreads();  // the previous stage's fragments have been read
-    store_stage();
-    __syncthreads();
-    if (k0 + BK < ke) load_stage(k0 + BK);  // next slices in flight during the products
+  auto multiply = [&](const uint16_t* As) {
+    const uint16_t* Bs = As + BM * LP;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i)
         af[i] = *reinterpret_cast<const bf16x8*>(&As[(arow + 32 * i) * LP + kk + kl]);
-        bfr[i] = *reinterpret_cast<const bf16x8*>(&Bs[(brow + 32 * i) * LP + kk + kl]);
-      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[(brow + 32 * j) * LP + kk + kl]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  if (kb < ke) {
+    load_slice(kb);
+    store_slice(stage0);
+  }
+  __syncthreads();
+  int s = 0;
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    const bool more = k0 + BK < ke;
+    if (more) load_slice(k0 + BK);  // in flight during the products
+    multiply(stage0 + s * kStage);
+    // the other stage was last read before the previous barrier
+    if (more) store_slice(stage0 + (s ^ 1) * kStage);
+    __syncthreads();
+    s ^= 1;
   }
 
   // epilogue: accumulator r of block (i, j) is C[m][n] with
-  // m = m0 + wm 64 + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, n = n0 + wn 64 + 32 j + lane % 32
+  // m = m0 + 128 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, n = n0 + 64 wn + 32 j + lane % 32
+  float* const c = g.C + blockIdx.z * g.split_stride;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn * 64 + 32 * j + (lane & 31);
     if (n >= g.N) continue;
-    float bn = 0.0f;
-    if constexpr (EPI == EPI_F32) {
-      if (g.bias != nullptr && blockIdx.z == 0) bn = bf16_to_f(g.bias[n]);
-    }
+    const float bn = (g.bias != nullptr && blockIdx.z == 0) ? bf16_to_f(g.bias[n]) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int m = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (m >= g.M) continue;
-        const int64_t o = static_cast<int64_t>(m) * g.ldc + n;
-        if constexpr (EPI == EPI_BF16) {
-          static_cast<uint16_t*>(g.C)[o] = f_to_bf16(acc[i][j][r]);
-        } else {
-          float* c = static_cast<float*>(g.C) + blockIdx.z * g.split_stride;
-          if constexpr (EPI == EPI_F32_ADD) c[o] += acc[i][j][r];
-          else c[o] = acc[i][j][r] + bn;
-        }
+        c[static_cast<int64_t>(m) * g.ldc + n] = acc[i][j][r] + bn;
       }
     }
   }

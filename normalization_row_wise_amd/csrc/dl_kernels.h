@@ -1,6 +1,7 @@
-// dl_kernels.h — the non-GEMM kernels of the fused linear JSD distillation loss:
-// the per-token loss and logit gradient over the vocabulary, transposes into the
-// K-contiguous layout the GEMM takes, and fixed-order reductions.
+// dl_kernels.h — the non-GEMM kernels of the fused linear JSD distillation loss: the
+// per-token statistics (log-sum-exps, divergence, gradient mean) over the vocabulary, the
+// logit gradient in the two layouts the gradient products take, a transpose into the
+// K-contiguous layout of the GEMM, and fixed-order reductions.
 //
 // Source: [distill] "perf(distillation): skip dW/dB calculation when parameters are
 // frozen", Summary (the loss differentiates the student head on every chunk unless it
@@ -17,7 +18,7 @@
 
 namespace dl {
 
-constexpr int JT = 1024;  // threads per token row
+constexpr int JT = 1024;  // threads per token row (statistics)
 
 // Sum over the workgroup (fixed tree order); every thread gets the result.
 __device__ __forceinline__ double block_sum(double v, double* sh) {
@@ -54,17 +55,6 @@ __device__ __forceinline__ void block_lse(float& m, double& s, float* shm, doubl
   __syncthreads();
 }
 
-struct JsdArgs {
-  float* zs; const float* zt; int64_t ldz;  // [rows][ldz] fp32 logits; zs becomes fp32 dz
-  uint16_t* gb; int64_t ldg;                // bf16 dz [rows][ldg], or null
-  double* jtok;                             // per-token J [rows]
-  int rows, V, vpad;                        // vpad: gb row length written (zeros past V)
-  float beta, inv_tau;
-  float grad_scale;                         // 1 / (tau * tokens): dL/dz = grad_scale * S (g - A)
-  int want_grad;                            // 0: loss only
-  int write_f32;                            // fp32 dz into zs (for dW / db)
-};
-
 // log(a e^x + b e^y) for a, b >= 0, stable for any x, y (a or b may be 0)
 __device__ __forceinline__ float log_mix(float la, float x, float lb, float y) {
   const float p = la + x, q = lb + y;
@@ -73,28 +63,72 @@ __device__ __forceinline__ float log_mix(float la, float x, float lb, float y) {
   return mx + log1pf(expf(-fabsf(p - q)));
 }
 
-// One workgroup per token row: three passes over the row's V logits (which the caches
-// mostly hold after the first): log-sum-exp of both rows (online max and sum), the
-// divergence and sum_u S_u g_u, then the gradient.
-__global__ __launch_bounds__(JT) void jsd_rows_kernel(JsdArgs a) {
+// e^x and ln x per vocabulary entry through the hardware's base-2 exponential and
+// logarithm (v_exp_f32 / v_log_f32 around a multiply by log2 e or ln 2): the rounding of
+// the product gives e^x a relative error of about |x| 2^-24, 1e-6 for the |x| < 30 that
+// carry weight here, and ln x an absolute error of about 2^-23 |ln x|.  The library
+// forms cost several times the instructions and made these kernels ALU-bound.
+__device__ __forceinline__ float fexp(float x) { return __expf(x); }
+__device__ __forceinline__ float flog(float x) { return __logf(x); }
+
+// ln M_v from ls = ln S_v, lt = ln T_v and their exponentials: ln of the mixture while it
+// is a normal float, else the stable form (both far in the tail: the terms it weighs are
+// below 1e-30).
+__device__ __forceinline__ float log_mixture(float b, float lb, float l1b, float s, float tt,
+                                             float ls, float lt) {
+  const float mix = b * tt + (1.0f - b) * s;
+  return mix > 1e-30f ? flog(mix) : log_mix(lb, lt, l1b, ls);
+}
+
+// Online (max, sum of exp(x - max)) over four values; x = -inf marks a value past V.
+__device__ __forceinline__ void lse_add4(float& m, double& s, const float x[4]) {
+  const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (m4 == -INFINITY) return;
+  if (m4 > m) {
+    s = s * static_cast<double>(fexp(m - m4));  // m = -inf: s = 0
+    m = m4;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (x[k] != -INFINITY) s += static_cast<double>(fexp(x[k] - m));
+}
+
+struct StatArgs {
+  const float* zs; const float* zt; int64_t ldz;  // [rows][ldz] fp32 logits (ldz % 4 == 0)
+  float* stats;                                   // [rows][4]: lse_s, lse_t, A, 0
+  double* jtok;                                   // per-token J [rows]
+  int rows, V;
+  float beta, inv_tau;
+};
+
+// One workgroup per token row, two passes over the row's logits with 16-byte loads:
+// log-sum-exp of both rows (online max and sum), then J and A = sum_u S_u g_u.
+__global__ __launch_bounds__(JT) void jsd_stats_kernel(StatArgs a) {
   __shared__ float shm[JT];
   __shared__ double shs[JT];
   const int row = blockIdx.x;
   if (row >= a.rows) return;
   const int t = threadIdx.x;
-  float* zs = a.zs + static_cast<int64_t>(row) * a.ldz;
-  const float* zt = a.zt + static_cast<int64_t>(row) * a.ldz;
+  const float4* zs = reinterpret_cast<const float4*>(a.zs + static_cast<int64_t>(row) * a.ldz);
+  const float4* zt = reinterpret_cast<const float4*>(a.zt + static_cast<int64_t>(row) * a.ldz);
   const int V = a.V;
+  const int nq = (V + 3) >> 2;
   const float it = a.inv_tau;
 
   float ms = -INFINITY, mt = -INFINITY;
   double ss = 0.0, st = 0.0;
-  for (int v = t; v < V; v += JT) {
-    const float xs = zs[v] * it, xt = zt[v] * it;
-    if (xs > ms) { ss = ss * static_cast<double>(expf(ms - xs)) + 1.0; ms = xs; }
-    else ss += static_cast<double>(expf(xs - ms));
-    if (xt > mt) { st = st * static_cast<double>(expf(mt - xt)) + 1.0; mt = xt; }
-    else st += static_cast<double>(expf(xt - mt));
+  for (int q = t; q < nq; q += JT) {
+    const float4 s4 = zs[q], t4 = zt[q];
+    const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, tv[4] = {t4.x, t4.y, t4.z, t4.w};
+    float xs[4], xt[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool in = 4 * q + k < V;
+      xs[k] = in ? sv[k] * it : -INFINITY;
+      xt[k] = in ? tv[k] * it : -INFINITY;
+    }
+    lse_add4(ms, ss, xs);
+    lse_add4(mt, st, xt);
   }
   block_lse(ms, ss, shm, shs);
   block_lse(mt, st, shm, shs);
@@ -104,54 +138,177 @@ __global__ __launch_bounds__(JT) void jsd_rows_kernel(JsdArgs a) {
   const float lb = logf(b), l1b = logf(1.0f - b);
 
   double jsum = 0.0, gsum = 0.0;
-  for (int v = t; v < V; v += JT) {
-    const float ls = zs[v] * it - lse_s, lt = zt[v] * it - lse_t;
-    const float lm = log_mix(lb, lt, l1b, ls);
-    const float s = expf(ls), tt = expf(lt);
-    const float g = (1.0f - b) * (ls - lm);
-    jsum += static_cast<double>(b * tt * (lt - lm) + (1.0f - b) * s * (ls - lm));
-    gsum += static_cast<double>(s * g);
+  for (int q = t; q < nq; q += JT) {
+    const float4 s4 = zs[q], t4 = zt[q];
+    const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (4 * q + k >= V) continue;
+      const float ls = sv[k] * it - lse_s, lt = tv[k] * it - lse_t;
+      const float s = fexp(ls), tt = fexp(lt);
+      const float lm = log_mixture(b, lb, l1b, s, tt, ls, lt);
+      const float g = (1.0f - b) * (ls - lm);
+      jsum += static_cast<double>(b * tt * (lt - lm) + (1.0f - b) * s * (ls - lm));
+      gsum += static_cast<double>(s * g);
+    }
   }
   jsum = block_sum(jsum, shs);
-  if (t == 0) a.jtok[row] = jsum;
-  if (!a.want_grad) return;
-  const float A = static_cast<float>(block_sum(gsum, shs));
-  uint16_t* gb = a.gb != nullptr ? a.gb + static_cast<int64_t>(row) * a.ldg : nullptr;
-  for (int v = t; v < V; v += JT) {
-    const float ls = zs[v] * it - lse_s, lt = zt[v] * it - lse_t;
-    const float lm = log_mix(lb, lt, l1b, ls);
-    const float s = expf(ls);
-    const float g = (1.0f - b) * (ls - lm);
-    const float dz = a.grad_scale * s * (g - A);
-    if (gb != nullptr) gb[v] = f_to_bf16(dz);
-    if (a.write_f32) zs[v] = dz;
+  const double A = block_sum(gsum, shs);
+  if (t == 0) {
+    a.jtok[row] = jsum;
+    float4 o;
+    o.x = lse_s; o.y = lse_t; o.z = static_cast<float>(A); o.w = 0.0f;
+    reinterpret_cast<float4*>(a.stats)[row] = o;
   }
-  if (gb != nullptr)
-    for (int v = V + t; v < a.vpad; v += JT) gb[v] = 0;  // K padding of the dx product
 }
 
-// out[c][r] = bf16(in[r][c]) for an R x C block, in 64 x 64 tiles through LDS; output
-// columns r in [R, Rpad) are written as zeros (K padding of a following product).
-template <typename TIN>
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const TIN* in, int64_t ldi, int R,
-                                                             int Cc, uint16_t* out, int64_t ldo,
-                                                             int Rpad) {
-  __shared__ uint16_t tile[64][65];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    uint16_t v = 0;
-    if (r < R && c < Cc) {
-      if constexpr (sizeof(TIN) == 2) v = static_cast<uint16_t>(in[static_cast<int64_t>(r) * ldi + c]);
-      else v = f_to_bf16(static_cast<float>(in[static_cast<int64_t>(r) * ldi + c]));
+// Logit-gradient tiles: 64 token rows x 256 vocabulary columns per workgroup of 256
+// threads; thread (q, w) = (t % 64, t / 64) takes columns 4q .. 4q + 3 of rows w + 4 i.
+constexpr int GR_ROWS = 64, GR_COLS = 256, GR_T = 256;
+constexpr int GR_PITCH = GR_COLS + 2;  // bf16 elements; spreads the column reads over banks
+
+struct GradArgs {
+  const float* zs; const float* zt; int64_t ldz;  // [rows][ldz] fp32 logits
+  const float* stats;                             // [rows][4] from jsd_stats_kernel
+  int rows, V;                                    // token rows of the chunk
+  float beta, inv_tau;
+  float grad_scale;                               // 1 / (tau * tokens)
+  uint16_t* gb; int64_t ldg; int vpad;            // bf16 dz [rows][ldg], zeros in [V, vpad); or null
+  uint16_t* gbt; int64_t ldt; int64_t tok0;       // bf16 dz^T: gbt[v][tok0 + r]; or null
+  int tok_rows;                                   // rows r < tok_rows written to gbt (zeros past rows)
+  float* dbp;                                     // [row tiles][V] column sums, or null
+};
+
+// dz for a tile, written as bf16 rows (the dx product's A operand), as bf16 columns of
+// dz^T through LDS (the dW product's A operand: 128 contiguous bytes per vocabulary row),
+// and as fp32 column sums of the tile's rows (db, fixed order).  The value of dz does not
+// depend on which of the three are written.
+__global__ __launch_bounds__(GR_T) void jsd_grad_kernel(GradArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[GR_ROWS * GR_PITCH];
+  __shared__ float colsum[4][GR_COLS];
+  const int t = threadIdx.x;
+  const int q = t & 63, w = t >> 6;
+  const int r0 = blockIdx.y * GR_ROWS;
+  const int c0 = blockIdx.x * GR_COLS;
+  const int v = c0 + 4 * q;
+  const float it = a.inv_tau, b = a.beta;
+  const float lb = logf(b), l1b = logf(1.0f - b);
+  float cs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int i = 0; i < GR_ROWS / 4; ++i) {
+    const int r = w + 4 * i;  // same in every lane of the wave
+    const int row = __builtin_amdgcn_readfirstlane(r0 + r);
+    float dz[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (row < a.rows) {
+      const float4 st = reinterpret_cast<const float4*>(a.stats)[row];
+      if (v < a.V) {
+        const float4 s4 = *reinterpret_cast<const float4*>(a.zs + static_cast<int64_t>(row) * a.ldz + v);
+        const float4 t4 = *reinterpret_cast<const float4*>(a.zt + static_cast<int64_t>(row) * a.ldz + v);
+        const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (v + k >= a.V) continue;
+          const float ls = sv[k] * it - st.x, lt = tv[k] * it - st.y;
+          const float s = fexp(ls), tt = fexp(lt);
+          const float lm = log_mixture(b, lb, l1b, s, tt, ls, lt);
+          const float g = (1.0f - b) * (ls - lm);
+          dz[k] = a.grad_scale * s * (g - st.z);
+          cs[k] += dz[k];
+        }
+      }
+      if (a.gb != nullptr && v < a.vpad) {
+        uint2 p;
+        p.x = static_cast<uint32_t>(f_to_bf16(dz[0])) | (static_cast<uint32_t>(f_to_bf16(dz[1])) << 16);
+        p.y = static_cast<uint32_t>(f_to_bf16(dz[2])) | (static_cast<uint32_t>(f_to_bf16(dz[3])) << 16);
+        *reinterpret_cast<uint2*>(a.gb + static_cast<int64_t>(row) * a.ldg + v) = p;
+      }
     }
-    tile[i][tx] = v;
+    if (a.gbt != nullptr) {
+      uint16_t* d = &tile[r * GR_PITCH + 4 * q];  // 4-byte aligned (GR_PITCH even)
+      reinterpret_cast<uint32_t*>(d)[0] =
+          static_cast<uint32_t>(f_to_bf16(dz[0])) | (static_cast<uint32_t>(f_to_bf16(dz[1])) << 16);
+      reinterpret_cast<uint32_t*>(d)[1] =
+          static_cast<uint32_t>(f_to_bf16(dz[2])) | (static_cast<uint32_t>(f_to_bf16(dz[3])) << 16);
+    }
+  }
+
+  if (a.dbp != nullptr) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) colsum[w][4 * q + k] = cs[k];
+  }
+  if (a.gbt != nullptr || a.dbp != nullptr) __syncthreads();
+
+  if (a.dbp != nullptr && r0 < a.rows) {
+    // column c of the tile: the four row groups' sums in order
+    const int vv = c0 + t;
+    if (vv < a.V)
+      a.dbp[static_cast<int64_t>(blockIdx.y) * a.V + vv] =
+          ((colsum[0][t] + colsum[1][t]) + colsum[2][t]) + colsum[3][t];
+  }
+  if (a.gbt != nullptr) {
+    // 256 columns x 8 groups of 8 tokens; lanes 8c' .. 8c' + 7 write one column's 128 bytes
+    const int lim = a.tok_rows - r0;  // tile rows to write
+#pragma unroll
+    for (int i = 0; i < (GR_COLS * GR_ROWS / 8) / GR_T; ++i) {
+      const int id = t + GR_T * i;
+      const int c = id >> 3, j = id & 7;
+      const int vv = c0 + c;
+      const int n = min(8, lim - 8 * j);
+      if (vv >= a.V || n <= 0) continue;
+      uint16_t e8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) e8[e] = tile[(8 * j + e) * GR_PITCH + c];
+      const int64_t tok = a.tok0 + r0 + 8 * j;
+      uint16_t* dst = a.gbt + static_cast<int64_t>(vv) * a.ldt + tok;
+      if (n == 8 && (tok & 7) == 0) {
+        u32x4 p;
+        p.x = e8[0] | (static_cast<uint32_t>(e8[1]) << 16);
+        p.y = e8[2] | (static_cast<uint32_t>(e8[3]) << 16);
+        p.z = e8[4] | (static_cast<uint32_t>(e8[5]) << 16);
+        p.w = e8[6] | (static_cast<uint32_t>(e8[7]) << 16);
+        *reinterpret_cast<u32x4*>(dst) = p;
+      } else {
+        for (int e = 0; e < n; ++e) dst[e] = e8[e];
+      }
+    }
+  }
+}
+
+// out[c][r] = in[r][c] (bf16) for an R x Cc block (Cc % 8 == 0, rows of `in` and `out`
+// 16-byte aligned), in 64 x 64 tiles through LDS with 16-byte global loads and stores;
+// output columns r in [R, Rpad) are written as zeros (Rpad % 8 == 0: the K padding of a
+// following product).
+constexpr int TP_PITCH = 72;  // bf16 elements: 16-byte aligned rows
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* in, int64_t ldi,
+                                                             int R, int Cc, uint16_t* out,
+                                                             int64_t ldo, int Rpad) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * TP_PITCH];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = t + 256 * i;
+    const int r = id >> 3, cc = (id & 7) * 8;
+    u32x4 p = {0u, 0u, 0u, 0u};
+    if (r0 + r < R && c0 + cc < Cc)
+      p = *reinterpret_cast<const u32x4*>(in + static_cast<int64_t>(r0 + r) * ldi + c0 + cc);
+    *reinterpret_cast<u32x4*>(&tile[r * TP_PITCH + cc]) = p;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < Cc && r < Rpad) out[static_cast<int64_t>(c) * ldo + r] = r < R ? tile[tx][i] : 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = t + 256 * i;
+    const int c = id >> 3, rr = (id & 7) * 8;
+    if (c0 + c >= Cc || r0 + rr >= Rpad) continue;
+    uint16_t e8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) e8[e] = tile[(rr + e) * TP_PITCH + c];  // zero past R
+    u32x4 p;
+    p.x = e8[0] | (static_cast<uint32_t>(e8[1]) << 16);
+    p.y = e8[2] | (static_cast<uint32_t>(e8[3]) << 16);
+    p.z = e8[4] | (static_cast<uint32_t>(e8[5]) << 16);
+    p.w = e8[6] | (static_cast<uint32_t>(e8[7]) << 16);
+    *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(c0 + c) * ldo + r0 + rr) = p;
   }
 }
 
@@ -168,13 +325,13 @@ __global__ __launch_bounds__(256) void split_sum_bf16_kernel(const float* part, 
   out[static_cast<int64_t>(m) * ldo + n] = f_to_bf16(s);
 }
 
-// db[v] (+)= sum over rows r = 0..R-1, in that order, of dz[r][v]
-__global__ __launch_bounds__(256) void colsum_rows_kernel(const float* dz, int64_t ldz, int R,
+// db[v] (+)= sum over rows r = 0..R-1, in that order, of p[r][v]
+__global__ __launch_bounds__(256) void colsum_rows_kernel(const float* p, int64_t ldp, int R,
                                                           int V, float* db, int accumulate) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   float s = 0.0f;
-  for (int r = 0; r < R; ++r) s += dz[static_cast<int64_t>(r) * ldz + v];
+  for (int r = 0; r < R; ++r) s += p[static_cast<int64_t>(r) * ldp + v];
   db[v] = accumulate ? db[v] + s : s;
 }
 
