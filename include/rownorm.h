@@ -69,7 +69,16 @@
 extern "C" {
 #endif
 
-typedef enum rn_dtype { RN_F32 = 0, RN_F16 = 1, RN_BF16 = 2 } rn_dtype;
+typedef enum rn_dtype {
+  RN_F32 = 0,
+  RN_F16 = 1,
+  RN_BF16 = 2,
+  /* Not types.  They make every 32-bit int a value of the enumeration, so that an
+   * unchecked value from a C or foreign-function caller is well defined in the library
+   * and reaches its check (RN_ERR_DTYPE). */
+  RN_DTYPE_RANGE_LO_ = -2147483647 - 1,
+  RN_DTYPE_RANGE_HI_ = 2147483647
+} rn_dtype;
 
 typedef enum rn_status {
   RN_OK = 0,
