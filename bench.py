@@ -55,10 +55,9 @@ def source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "normalization_row_wise_amd", "csrc")
     for f in sorted(f for f in os.listdir(csrc) if f.startswith("rn_")) + [
-            "../../../include/rownorm.h"]:
+            "../../include/rownorm.h"]:
         path = os.path.normpath(os.path.join(csrc, f))
-        if os.path.isfile(path):
-            h.update(open(path, "rb").read())
+        h.update(open(path, "rb").read())  # a missing file is an error, not a silent skip
     return h.hexdigest()[:16]
 
 
@@ -501,6 +500,9 @@ def main():
     ap.add_argument("--event-steps", type=int, default=100)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--distill-only", action="store_true",
+                    help="only time the distillation loss sizes (profiler runs); prints "
+                         "{\"distill_jsd\": ...}")
     args = ap.parse_args()
 
     if args.calibrate_copy:
@@ -527,6 +529,11 @@ def main():
     import __graft_entry__
     __graft_entry__.ensure_built()
     import normalization_row_wise_amd as rn
+
+    if args.distill_only:
+        out = {dwl.name: measure_distill(dwl, args.rounds, torch) for dwl in workloads.DISTILL_CONFIGS}
+        print(json.dumps({"distill_jsd": out}), flush=True)
+        return
 
     wl = workloads.BY_NAME[args.config]
     m = measure(wl, args.steps, args.warmup, args.rounds, rn, torch, args.event_steps, args.eager)
