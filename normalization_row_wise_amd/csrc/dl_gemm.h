@@ -17,7 +17,7 @@
 // registers before the products of the current stage and written to the other stage
 // after them, so one barrier per slice suffices.  Per CU and slice the LDS serves 192 KiB
 // of fragment reads and 64 KiB of stores against 2 x 32 MFMAs per SIMD; the 128 x 128
-// tile of four waves needed a third more LDS traffic per product and was 15-20 % slower
+// tile of four waves needed a third more LDS traffic per product and was 11-20 % slower
 // on these shapes.  The two stages (144 KiB) leave room for one workgroup per CU.
 // Loads go through buffer resources: rows past M (N) and columns past K read zero, so
 // ragged edges need no branches; K must be a multiple of 8, and 256 rows of A or B must
