@@ -25,7 +25,8 @@
  * rounded to bf16 before the two gradient products (dx, dW), whose accumulation is fp32;
  * dx is stored in bf16, dW and db in fp32, the loss in fp32.  Every reduction has a
  * fixed order: results are bitwise reproducible, and the loss and dx do not depend on
- * which parameter gradients are requested.
+ * which parameter gradients are requested.  With beta = 0 or 1 the mixture is S or T
+ * itself: the loss and every gradient are then exactly zero.
  *
  * Schedule: per chunk, the two logits products, the per-token statistics, the logit
  * gradient and the dx product; dW is one product over all tokens after the last chunk

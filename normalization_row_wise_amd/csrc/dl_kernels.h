@@ -73,9 +73,12 @@ __device__ __forceinline__ float flog(float x) { return __logf(x); }
 
 // ln M_v from ls = ln S_v, lt = ln T_v and their exponentials: ln of the mixture while it
 // is a normal float, else the stable form (both far in the tail: the terms it weighs are
-// below 1e-30).
+// below 1e-30).  At the end points of the weight the mixture is one of the two
+// distributions and its logarithm is known exactly, so J and the gradient are exactly 0.
 __device__ __forceinline__ float log_mixture(float b, float lb, float l1b, float s, float tt,
                                              float ls, float lt) {
+  if (b == 0.0f) return ls;  // M = S
+  if (b == 1.0f) return lt;  // M = T
   const float mix = b * tt + (1.0f - b) * s;
   return mix > 1e-30f ? flog(mix) : log_mix(lb, lt, l1b, ls);
 }

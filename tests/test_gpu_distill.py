@@ -107,6 +107,22 @@ def test_frozen_head_changes_nothing_else(wl):
     assert dxw is None and torch.equal(dww, dw)
 
 
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_mixture_weight_end_points(beta):
+    """beta = 0 or 1: the mixture is the student's (teacher's) distribution itself, so J
+    and every gradient vanish (the oracle's closed form); the kernels then take ln M as
+    ln S (ln T) and return exact zeros."""
+    wl = workloads.DistillWorkload(f"d200_h64_v3000_beta{beta:g}", 200, 64, 64, 3000, 64,
+                                   beta=beta, bias=True, seed=11)
+    _say(wl.name)
+    t = workloads.generate_distill(wl)
+    loss, dx, dw, db = _run(wl, t)
+    o = _oracle(wl, t)
+    assert abs(o["loss"]) < 1e-12 and np.abs(o["dx"]).max() < 1e-12
+    assert float(loss[0]) == 0.0
+    assert not dx.float().any() and not dw.any() and not db.any()
+
+
 def test_workspace_smaller_for_a_frozen_head():
     from normalization_row_wise_amd import distill
     wl = workloads.DISTILL_4096x4096_V128256

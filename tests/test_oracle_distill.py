@@ -130,6 +130,10 @@ def check_invariants(impl):
         # J_beta(S, T) = J_(1-beta)(T, S)
         jr, _ = impl.jsd_rows(zt, zs, 1 - beta, 1.0)
         assert rel(jr, j) < 1e-12, ("swap", beta)
+    # mixture weight 0 or 1: M is S or T itself, so J and its gradient vanish
+    for beta in (0.0, 1.0):
+        j, dz = impl.jsd_rows(zs, zt, beta, 1.0)
+        assert np.abs(j).max() < 1e-14 and np.abs(dz).max() < 1e-14, ("end point", beta)
     # temperature: tau on the logits equals logits divided by tau
     for tau in (0.5, 3.0):
         jt, dzt = impl.jsd_rows(zs, zt, 0.4, tau)
