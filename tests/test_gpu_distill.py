@@ -123,6 +123,21 @@ def test_mixture_weight_end_points(beta):
     assert not dx.float().any() and not dw.any() and not db.any()
 
 
+def test_empty_batch():
+    """No tokens: the loss is 0 (the mean over an empty batch is taken as 0, as in the
+    oracle) and dW and db are written as zeros over their NaN fill; dx is empty."""
+    wl = workloads.DistillWorkload("d0_h64_v300_bias", 0, 64, 64, 300, 16, bias=True, seed=12)
+    _say(wl.name)
+    t = workloads.generate_distill(wl)
+    dw = torch.full((wl.V, wl.H), float("nan"), device=gp.dev())
+    db = torch.full((wl.V,), float("nan"), device=gp.dev())
+    loss, dx, dw, db = _run(wl, t, dw=dw, db=db)
+    o = _oracle(wl, t)
+    assert o["loss"] == 0.0 and float(loss[0]) == 0.0
+    assert tuple(dx.shape) == (0, wl.H)
+    assert not dw.any() and not db.any()
+
+
 def test_workspace_smaller_for_a_frozen_head():
     from normalization_row_wise_amd import distill
     wl = workloads.DISTILL_4096x4096_V128256
