@@ -26,11 +26,14 @@ namespace {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Split of the dx product's K (= V) so that it has about two workgroups per CU (one
-// fits at a time: the GEMM takes 144 KiB of LDS).
+// Split of the dx product's K (= V) so that it has about one workgroup per CU (one fits
+// at a time: the GEMM takes 144 KiB of LDS), a single round.  At 1024 tokens x 4096:
+// 4 splits against 8 (two rounds, twice the fp32 partial slices to write and sum) took
+// the call from 20.50 to 20.31 ms (trainable, V = 128256) and 15.89 to 15.73 ms
+// (frozen); 6 splits (a round and a half) was slower than both.
 inline int dx_splits(int64_t chunk, int64_t H) {
   const int64_t tiles = cdiv(chunk, BM) * cdiv(H, BN);
-  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, 512 / std::max<int64_t>(1, tiles))));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, 256 / std::max<int64_t>(1, tiles))));
 }
 
 // Byte offsets of the workspace parts (each 256-byte aligned); total in `end`.
