@@ -90,11 +90,23 @@ __device__ __forceinline__ bool tile_of(int id, int mt, int nt, int& mi, int& ni
   return ni < nt;
 }
 
-__global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmArgs g) {
+// One launch computes one product, or two independent ones (the two heads' logits of a
+// chunk): workgroups below `grid0` take p[0], the others p[1].  Each product's share of
+// the grid is a multiple of 8 workgroups, so its placement over the XCDs is the same as
+// in a launch of its own; the second product fills the first one's last partial round.
+struct GemmLaunch {
+  GemmArgs p[2];
+  int grid0;  // workgroups of p[0] (all of them for a single product)
+};
+
+__global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmLaunch gl) {
   extern __shared__ u32x4 gemm_lds[];
   uint16_t* const stage0 = reinterpret_cast<uint16_t*>(gemm_lds);
+  const bool second = static_cast<int>(blockIdx.x) >= gl.grid0;  // uniform per workgroup
+  const GemmArgs g = second ? gl.p[1] : gl.p[0];
+  const int id = static_cast<int>(blockIdx.x) - (second ? gl.grid0 : 0);
   int mi, ni;
-  if (!tile_of(blockIdx.x, g.mt, g.nt, mi, ni)) return;  // uniform per workgroup
+  if (!tile_of(id, g.mt, g.nt, mi, ni)) return;  // uniform per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
