@@ -113,10 +113,14 @@ bool allow_gemm_lds() {
 }
 
 // Arguments of C[M x N] = A[M x K] B[N x K]^T (+ bias) with `splits` K ranges written to
-// slices of C; `wgs` receives the product's workgroups per K range.
+// slices of C; `wgs` receives the product's workgroups per K range.  The tiles that share
+// a tile of the larger operand run on one XCD (its L2 then fetches that tile once): the
+// row tiles of a column tile when B is the larger (logits, dx), the column tiles of a
+// row tile when A is (dW: 4.37 -> 4.27 ms at 128256 x 4096 x 4096, traced).
 GemmArgs gemm_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
                    int64_t ldc, int64_t split_stride, const uint16_t* bias, int64_t M, int64_t N,
                    int64_t K, int splits, int64_t& wgs) {
+  const int by_rows = M > N ? 1 : 0;
   GemmArgs g{};
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.split_stride = split_stride; g.bias = bias;
@@ -124,7 +128,8 @@ GemmArgs gemm_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ld
   g.k_per_split = static_cast<int>(rup(cdiv(K, splits), BK));
   g.mt = static_cast<int>(cdiv(M, BM));
   g.nt = static_cast<int>(cdiv(N, BN));
-  wgs = 8 * cdiv(g.nt, 8) * g.mt;
+  g.by_rows = by_rows;
+  wgs = by_rows ? 8 * cdiv(g.mt, 8) * g.nt : 8 * cdiv(g.nt, 8) * g.mt;
   return g;
 }
 

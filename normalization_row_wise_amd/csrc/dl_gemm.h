@@ -26,7 +26,8 @@
 // Placement.  Workgroups are dealt to the 8 XCDs round-robin by id.  The ids are mapped
 // so that all row tiles of one column tile of C run on the same XCD at about the same
 // time: the column tile of B is then fetched from HBM once into that XCD's L2 and reused
-// by every row tile.
+// by every row tile.  With `by_rows` the roles swap (all column tiles of one row tile on
+// one XCD), for products whose A is the larger operand.
 //
 // Split K (grid.z > 1): workgroup z adds K range z and writes its own fp32 slice of C;
 // a fixed-order sum of the slices follows (deterministic).
@@ -50,6 +51,7 @@ struct GemmArgs {
   int M, N, K;
   int k_per_split;                  // multiple of 64
   int mt, nt;                       // row / column tiles of C
+  int by_rows;                      // placement: 0 column tiles per XCD, 1 row tiles
 };
 
 constexpr int GT = 512;            // threads per workgroup
@@ -82,9 +84,14 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f) {
 
 // Tile (mi, ni) of workgroup `id` (see Placement).  Returns false for the ids that
 // round the grid up to a multiple of 8 column tiles.
-__device__ __forceinline__ bool tile_of(int id, int mt, int nt, int& mi, int& ni) {
+__device__ __forceinline__ bool tile_of(int id, int mt, int nt, int by_rows, int& mi, int& ni) {
   const int x = id & 7;
   const int q = id >> 3;
+  if (by_rows) {
+    ni = q % nt;
+    mi = (q / nt) * 8 + x;
+    return mi < mt;
+  }
   mi = q % mt;
   ni = (q / mt) * 8 + x;
   return ni < nt;
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(GT) void gemm_nt_kernel(GemmLaunch gl) {
   const GemmArgs g = second ? gl.p[1] : gl.p[0];
   const int id = static_cast<int>(blockIdx.x) - (second ? gl.grid0 : 0);
   int mi, ni;
-  if (!tile_of(id, g.mt, g.nt, mi, ni)) return;  // uniform per workgroup
+  if (!tile_of(id, g.mt, g.nt, g.by_rows, mi, ni)) return;  // uniform per workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
