@@ -111,6 +111,7 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
   // Load this thread's elements through a buffer resource covering the row: offsets
   // at or past the resource's byte count read as zero (row tails, rows past M), so
   // there is no per-access branch and no 64-bit address arithmetic.
+  template <int POL = 0>
   __device__ __forceinline__ void load(rsrc_t rs, int t, int T) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
@@ -119,16 +120,16 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
         static_assert(WPL % 4 == 0, "vector access is a whole number of 16-byte loads");
 #pragma unroll
         for (int q = 0; q < WPL / 4; ++q) {
-          const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + q * 16, 0, 0);
+          const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + q * 16, 0, POL);
           w[l * WPL + q * 4 + 0] = v.x;
           w[l * WPL + q * 4 + 1] = v.y;
           w[l * WPL + q * 4 + 2] = v.z;
           w[l * WPL + q * 4 + 3] = v.w;
         }
       } else if constexpr (B == 2) {
-        w[l] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+        w[l] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, POL);
       } else {
-        w[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        w[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, POL);
       }
     }
   }
@@ -141,6 +142,7 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
     const int col = (l * T + t) * VE;
     return col < N ? base + static_cast<uint32_t>(col * B) : 0x80000000u;
   }
+  template <int POL = 0>
   __device__ __forceinline__ void load_at(rsrc_t rs, uint32_t base, int t, int T, int N) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
@@ -149,19 +151,20 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
         static_assert(WPL % 4 == 0, "vector access is a whole number of 16-byte loads");
 #pragma unroll
         for (int q = 0; q < WPL / 4; ++q) {
-          const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + q * 16, 0, 0);
+          const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + q * 16, 0, POL);
           w[l * WPL + q * 4 + 0] = v.x;
           w[l * WPL + q * 4 + 1] = v.y;
           w[l * WPL + q * 4 + 2] = v.z;
           w[l * WPL + q * 4 + 3] = v.w;
         }
       } else if constexpr (B == 2) {
-        w[l] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+        w[l] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, POL);
       } else {
-        w[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        w[l] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, POL);
       }
     }
   }
+  template <int POL = 0>
   __device__ __forceinline__ void store_at(rsrc_t rs, uint32_t base, int t, int T, int N) const {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
@@ -171,17 +174,18 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
         for (int q = 0; q < WPL / 4; ++q) {
           const v4u v = {w[l * WPL + q * 4], w[l * WPL + q * 4 + 1], w[l * WPL + q * 4 + 2],
                          w[l * WPL + q * 4 + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off + q * 16, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off + q * 16, 0, POL);
         }
       } else if constexpr (B == 2) {
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[l]), rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[l]), rs, off, 0, POL);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b32(w[l], rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(w[l], rs, off, 0, POL);
       }
     }
   }
 
   // Store the words as they are; stores past the resource's byte count are dropped.
+  template <int POL = 0>
   __device__ __forceinline__ void store_raw(rsrc_t rs, int t, int T) const {
 #pragma unroll
     for (int l = 0; l < NL; ++l) {
@@ -191,12 +195,12 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
         for (int q = 0; q < WPL / 4; ++q) {
           const v4u v = {w[l * WPL + q * 4], w[l * WPL + q * 4 + 1], w[l * WPL + q * 4 + 2],
                          w[l * WPL + q * 4 + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off + q * 16, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, off + q * 16, 0, POL);
         }
       } else if constexpr (B == 2) {
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[l]), rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(w[l]), rs, off, 0, POL);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b32(w[l], rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(w[l], rs, off, 0, POL);
       }
     }
   }
