@@ -180,10 +180,8 @@ inline int narrow_team(int64_t N, bool vec, int64_t max_ld, int eb) {
 
 // kind: 0 forward, 1 backward with parameter grads, 2 backward without.
 // ngrads: parameter gradients computed (kind 1).  vec: 16-byte accesses possible;
-// max_ld: the widest row stride of the call's row tensors; xg: the backward's exact-product
-// path (16-bit weight, nothing added to it).
-Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec, int64_t max_ld,
-           bool xg = false) {
+// max_ld: the widest row stride of the call's row tensors.
+Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec, int64_t max_ld) {
   Shape s;
   const int eb = elem_bytes(xt);
   if (const int ts = narrow_team(N, vec, max_ld, eb)) {
@@ -209,18 +207,7 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
     s.P = kind == 1 ? static_cast<int>(s.grid) : 0;
     return s;
   }
-  // RMSNorm backward over at least 32 rows per partial row, 16-bit rows on the exact-
-  // product path, N in (7168, 8192]: one 512-thread team per row at V = 16 (two waves
-  // per SIMD in the trainable launch, dW in registers) instead of a 256-thread team at
-  // V = 32.  The trainable and frozen forms take the same layout.  Graph-replayed steps,
-  // trainable / frozen, us: 8192 x 8192 bf16 133.5 / 121.9 -> 130.6 / 120.3, 16384 x 8192
-  // 251.8 / 235.7 -> 247.6 / 235.7, 8192 x 8000 131.0 / 119.9 -> 128.6 / 118.9, fp16
-  // 8192 x 8192 131.3 / 121.1 -> 130.4 / 121.1.  Level at 2048 and 4096 rows, slower
-  // at 512 rows (22.4 -> 25.9), with an offset (Gemma, 131.6 -> 132.0) and with an fp32
-  // weight (4096 x 8192: 77.2 -> 79.2).
-  const bool rms_team512 = kind >= 1 && op == OP_RMS && eb == 2 && vec && xg &&
-                           M >= 32 * kMaxPartials && team_of(N, 16) == 512;
-  s.v = rms_team512 ? 16 : pick_v(kind, op, N, eb);
+  s.v = pick_v(kind, op, N, eb);
   s.team = static_cast<int>(team_of(N, s.v));
   const int wg_cap = max_wg(kind, s.v, eb);
   const int r_cap = wg_cap / s.team;
@@ -249,14 +236,13 @@ Shape plan(int kind, int op, int64_t M, int64_t N, int xt, int ngrads, bool vec,
         R = 256 / s.team;
       R = std::max(1, std::min(R, r_cap));
       s.shmem = block;
-      // RMSNorm with one 256-thread team per workgroup (or the 512-thread team above): dW
-      // accumulates in registers (one
+      // RMSNorm with one 256-thread team per workgroup: dW accumulates in registers (one
       // workgroup per CU leaves the VGPRs: 162 at V = 32) instead of a read-modify-write
       // of its LDS block per row.  Trainable 8192 x 8192 bf16 backward (both kernels,
       // events around the call) 91.6 -> 88.5 us.  Slower with several teams to combine
       // (LayerNorm 2048 x 4096 23.9 -> 36.1 us) and for the fused add's three-row ring
       // (2048 x 8192 37.6 -> 39.9 us), so only here.
-      if (op == OP_RMS && R == 1 && (s.team == 256 || rms_team512) && (s.v == 16 || s.v == 32)) {
+      if (op == OP_RMS && R == 1 && s.team == 256 && (s.v == 16 || s.v == 32)) {
         s.acc = 0;
         s.shmem = 0;
       }
@@ -549,9 +535,7 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
   const int kind = ngrads > 0 ? 1 : 2;
   const bool aliased = dx == dy || dx == x || (dres != nullptr && dx == dres);
   const Split sp = split_plan(op, M, N, eb, vec, aliased);
-  // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it
-  const bool xg = (wt != RN_F32) && (op == OP_LN || offset == 0.0f);
-  const Shape s = plan(kind, op, M, N, xt, ngrads, vec, max_ld, xg);
+  const Shape s = plan(kind, op, M, N, xt, ngrads, vec, max_ld);
   // partial rows: one per workgroup, or one per row when rows are split
   const int P = sp.wgs > 0 ? static_cast<int>(M) : s.P;
   BwdArgs a{};
@@ -580,6 +564,8 @@ static int backward(int op, const void* dy, int64_t lddy, const void* x, int64_t
     l.shmem = 0;
   }
   const int dxt = to_dt(xt), dwt = to_dt(wt);
+  // exact fp32 products g = dy * w when the weight is 16-bit and nothing is added to it
+  const bool xg = (wt != RN_F32) && (op == OP_LN || offset == 0.0f);
   const BwdVariant bv{dw != nullptr, db != nullptr, xg, s.acc};
   int ls;
   if (op == OP_RMS) ls = launch_bwd_rms(dxt, dwt, bv, l, a, st);

@@ -111,9 +111,8 @@ def test_frozen_dx_bit_identical_and_dw_unchanged(op, io):
 
 
 # Shapes whose frozen backward once took its own row layout (a frozen-only V for wide
-# rows and for the fused add): the layout now depends on the operation, the shape, the
-# types and the weight path only, never on the gradients requested, so dx is
-# bit-identical by construction, fp32 outputs included.
+# rows and for the fused add): the layout now depends on the operation, N and the type
+# only, so dx is bit-identical by construction, fp32 outputs included.
 @pytest.mark.parametrize("case", [
     ("fused_add_rmsnorm", 2048, 8192, "bf16", "bf16"),
     ("fused_add_rmsnorm", 300, 8192, "fp32", "fp32"),
@@ -178,8 +177,7 @@ def test_wide_rows_one_row_ahead(wl):
 
 # RMSNorm over 2048 rows or more (the fused add over 8192 or more), with teams of 64,
 # 128 or 256 threads that cover at least 2048 elements: the trainable backward runs
-# 256-thread workgroups of 4, 2 or 1 teams (and, for the widest 16-bit RMSNorm rows from
-# 8192 rows on, one 512-thread team).  Row counts leave the last workgroups short; N is ragged where the team allows.
+# 256-thread workgroups of 4, 2 or 1 teams.  Row counts leave the last workgroups short; N is ragged where the team allows.
 RMS_TALL = [
     workloads.small("rmsnorm", 2100, 1500, "bf16", seed=101),    # teams of 64 (V = 32)
     workloads.small("rmsnorm", 2051, 4096, "bf16", seed=102),    # teams of 128
@@ -190,9 +188,8 @@ RMS_TALL = [
     workloads.small("fused_add_rmsnorm", 8193, 4096, "bf16", offset=1.0, weight="gemma",
                     seed=105),
     workloads.small("fused_add_rmsnorm", 8200, 2000, "fp16", seed=106),
-    # RMSNorm from 8192 rows with 16-bit rows and weight, no offset, N in (7168, 8192]:
-    # one 512-thread team per row at 16 elements per lane, trainable and frozen (N ragged
-    # against the team; 33 or 32 rows per workgroup)
+    # RMSNorm from 8192 rows with rows up to 8192 wide: one 256-thread team per workgroup
+    # (N ragged against the team; 33 or 32 rows per workgroup)
     workloads.small("rmsnorm", 8193, 7176, "bf16", seed=107),
     workloads.small("rmsnorm", 8200, 8000, "fp16", seed=108),
 ]
