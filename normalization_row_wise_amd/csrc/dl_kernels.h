@@ -19,6 +19,7 @@
 namespace dl {
 
 constexpr int JT = 1024;  // threads per token row (statistics)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Sum over the workgroup (fixed tree order); every thread gets the result.
 __device__ __forceinline__ double block_sum(double v, double* sh) {
@@ -205,9 +206,12 @@ __global__ __launch_bounds__(GR_T) void jsd_grad_kernel(GradArgs a) {
     if (row < a.rows) {
       const float4 st = reinterpret_cast<const float4*>(a.stats)[row];
       if (v < a.V) {
-        const float4 s4 = *reinterpret_cast<const float4*>(a.zs + static_cast<int64_t>(row) * a.ldz + v);
-        const float4 t4 = *reinterpret_cast<const float4*>(a.zt + static_cast<int64_t>(row) * a.ldz + v);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, tv[4] = {t4.x, t4.y, t4.z, t4.w};
+        // the logits' last reader: non-temporal loads
+        const f32x4 s4 = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(a.zs + static_cast<int64_t>(row) * a.ldz + v));
+        const f32x4 t4 = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(a.zt + static_cast<int64_t>(row) * a.ldz + v));
+        const float sv[4] = {s4[0], s4[1], s4[2], s4[3]}, tv[4] = {t4[0], t4[1], t4[2], t4[3]};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if (v + k >= a.V) continue;
@@ -323,8 +327,8 @@ __global__ __launch_bounds__(256) void split_sum_bf16_kernel(const float* part, 
   if (i >= static_cast<int64_t>(M) * N) return;
   const int m = static_cast<int>(i / N), n = static_cast<int>(i % N);
   const int64_t o = static_cast<int64_t>(m) * ldp + n;
-  float s = part[o];
-  for (int z = 1; z < S; ++z) s += part[z * stride + o];
+  float s = __builtin_nontemporal_load(&part[o]);  // the partial slices' last reader
+  for (int z = 1; z < S; ++z) s += __builtin_nontemporal_load(&part[z * stride + o]);
   out[static_cast<int64_t>(m) * ldo + n] = f_to_bf16(s);
 }
 
