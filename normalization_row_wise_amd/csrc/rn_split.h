@@ -214,7 +214,7 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
     const rsrc_t ry = row_rsrc<SX>(p.y, p.ldy, row, N);
     auto emit = [&](Own& in, int a) {
       summed(in.x, in.r);
-      if constexpr (OP == OP_FADD) in.x.store_raw(row_rsrc<SX>(p.ro, p.ldro, row, N), a, 0);
+      if constexpr (OP == OP_FADD) in.x.template store_raw<kNonTemporal>(row_rsrc<SX>(p.ro, p.ldro, row, N), a, 0);
       float o[EVE];
 #pragma unroll
       for (int i = 0; i < EVE; ++i) {
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(SPLIT_WG) void split_fwd_kernel(FwdArgs p) {
       }
       FX yf;
       yf.pack(o);
-      yf.store_raw(ry, a, 0);
+      yf.template store_raw<kNonTemporal>(ry, a, 0);
     };
     emit(first, s_first * SPLIT_WG + t);
     if constexpr (MORE) {
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(SPLIT_WG) void split_bwd_kernel(BwdArgs p) {
       }
       FX of;
       of.pack(o);
-      of.store_raw(rdx, a, 0);
+      of.template store_raw<kNonTemporal>(rdx, a, 0);
       if constexpr (CDW) put(p.pw, dwp, a);
       if constexpr (CDB) put(p.pb, dbp, a);
     };
