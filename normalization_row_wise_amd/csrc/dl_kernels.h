@@ -122,8 +122,9 @@ __global__ __launch_bounds__(JT) void jsd_stats_kernel(StatArgs a) {
   float ms = -INFINITY, mt = -INFINITY;
   double ss = 0.0, st = 0.0;
   for (int q = t; q < nq; q += JT) {
-    const float4 s4 = zs[q], t4 = zt[q];
-    const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, tv[4] = {t4.x, t4.y, t4.z, t4.w};
+    const f32x4 s4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zs) + q);
+    const f32x4 t4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zt) + q);
+    const float sv[4] = {s4[0], s4[1], s4[2], s4[3]}, tv[4] = {t4[0], t4[1], t4[2], t4[3]};
     float xs[4], xt[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -143,8 +144,9 @@ __global__ __launch_bounds__(JT) void jsd_stats_kernel(StatArgs a) {
 
   double jsum = 0.0, gsum = 0.0;
   for (int q = t; q < nq; q += JT) {
-    const float4 s4 = zs[q], t4 = zt[q];
-    const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, tv[4] = {t4.x, t4.y, t4.z, t4.w};
+    const f32x4 s4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zs) + q);
+    const f32x4 t4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(zt) + q);
+    const float sv[4] = {s4[0], s4[1], s4[2], s4[3]}, tv[4] = {t4[0], t4[1], t4[2], t4[3]};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (4 * q + k >= V) continue;
