@@ -110,7 +110,8 @@ template <int DT, int V, int EVE, bool VEC> struct Frag {
 
   // Load this thread's elements through a buffer resource covering the row: offsets
   // at or past the resource's byte count read as zero (row tails, rows past M), so
-  // there is no per-access branch and no 64-bit address arithmetic.
+  // there is no per-access branch and no 64-bit address arithmetic.  POL is the buffer
+  // instructions' cache-policy operand (0 default, 2 non-temporal), here and below.
   template <int POL = 0>
   __device__ __forceinline__ void load(rsrc_t rs, int t, int T) {
 #pragma unroll
