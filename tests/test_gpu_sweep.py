@@ -81,3 +81,82 @@ def test_random_problem(wl):
     frozen = gp.run_gpu(wl, t, dw=False, db=False)
     bits = torch.int32 if wl.io == "fp32" else torch.int16
     assert torch.equal(g["dx"].view(bits), frozen["dx"].view(bits))
+
+
+# ---- the same with padded rows ---------------------------------------------------------
+# Every row tensor lives inside a wider allocation (row stride N + pad, pad 0..64) at a
+# lead offset of 0..pad elements, so row pitch and base alignment vary independently; dx
+# overwrites dy (the fused add: dres) half the time.
+
+def _strided_draws(n=32, seed=0x57D):
+    rng = np.random.default_rng(seed)
+    base = _draws(n, seed)
+    out = []
+    for wl in base:
+        M = max(1, min(wl.M, (4 << 20) // wl.N))
+        w2 = workloads.small(wl.op, M, wl.N, wl.io, wl.wt, eps=wl.eps, offset=wl.offset,
+                             weight=wl.weight, bias=wl.bias, dres=wl.dres, seed=wl.seed + 500)
+        pad = int(rng.integers(0, 65))
+        leads = [int(rng.integers(0, pad + 1)) for _ in range(4)]
+        out.append((w2, pad, leads, bool(rng.integers(2))))
+    return out
+
+
+STRIDED = _strided_draws()
+
+
+def _padded(src, pad, lead):
+    M, N = src.shape
+    big = torch.zeros(M, N + pad, dtype=src.dtype, device=gp.dev())
+    v = big[:, lead:lead + N]
+    v.copy_(src.to(gp.dev()))
+    return v
+
+
+def _run_padded(wl, t, pad, leads, inplace, trainable):
+    import normalization_row_wise_amd as rn
+    w = t["w"].to(gp.dev())
+    x = _padded(t["x"], pad, leads[0])
+    dy = _padded(t["dy"], pad, leads[1])
+    dw = True if trainable else None
+    out = {}
+    if wl.op == "rmsnorm":
+        out["y"], out["rstd"] = rn.rmsnorm_fwd(x, w, t["eps"], t["offset"])
+        out["dx"], out["dw"] = rn.rmsnorm_bwd(dy, x, w, t["eps"], t["offset"],
+                                              dx=dy if inplace else None, dw=dw)
+    elif wl.op == "layernorm":
+        b = t["b"].to(gp.dev()) if "b" in t else None
+        out["y"], out["mean"], out["rstd"] = rn.layernorm_fwd(x, w, b, t["eps"])
+        out["dx"], out["dw"], out["db"] = rn.layernorm_bwd(dy, x, w, t["eps"],
+                                                           dx=dy if inplace else None, dw=dw,
+                                                           db=True if trainable else None)
+    else:
+        res = _padded(t["residual"], pad, leads[2])
+        out["y"], out["residual_out"], out["rstd"] = rn.fused_add_rmsnorm_fwd(
+            x, res, w, t["eps"], t["offset"])
+        dres = _padded(t["dres"], pad, leads[3]) if "dres" in t else None
+        target = (dres if dres is not None else dy) if inplace else None
+        out["dx"], out["dw"] = rn.fused_add_rmsnorm_bwd(dy, out["residual_out"], w, t["eps"],
+                                                        t["offset"], dres, dx=target, dw=dw)
+        if inplace:
+            assert out["dx"].data_ptr() == target.data_ptr()
+    if inplace and wl.op != "fused_add_rmsnorm":
+        assert out["dx"].data_ptr() == dy.data_ptr()
+    torch.cuda.synchronize()
+    return {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("case", STRIDED,
+                         ids=lambda c: f"{c[0].name}_pad{c[1]}_lead{'-'.join(map(str, c[2]))}"
+                                       f"{'_inplace' if c[3] else ''}")
+def test_random_padded_problem(case):
+    wl, pad, leads, inplace = case
+    print("[case] padded sweep", wl.name, f"pad={pad} leads={leads} inplace={inplace}",
+          flush=True)
+    t = workloads.generate(wl)
+    g = _run_padded(wl, t, pad, leads, inplace, trainable=True)
+    fails = gp.compare_all_rows(wl, g, t)
+    assert not fails, "\n".join(fails)
+    frozen = _run_padded(wl, t, pad, leads, inplace, trainable=False)
+    bits = torch.int32 if wl.io == "fp32" else torch.int16
+    assert torch.equal(g["dx"].view(bits), frozen["dx"].view(bits))
