@@ -10,6 +10,8 @@ Gates (the tolerances this path is held to):
   * rstd / mean (fp32): relative L2 <= 1e-6.
   * residual_out: bit-exact (x + residual of two stored values, rounded once).
   * dx with frozen parameters: bit-identical to dx with trainable parameters.
+  * fused linear JSD loss: loss within 2e-4 relative, dx within 4e-3 and dW within 3e-3
+    relative L2, dB within 1e-4.
 Every row of every output is compared (check() runs the oracle on chunks of rows).
 Relative L2 is ||a - o||_2 / max(||o||_2, 1e-30) in fp64 (the metric of the accuracy
 reproduction on "fix(cutedsl): fuse Gemma RMSNorm weight offset in FP32").
@@ -27,6 +29,11 @@ MAX_ULP16 = 1
 REL_F32 = 1e-5
 REL_GRAD = 1e-5
 REL_STAT = 1e-6
+# fused linear JSD distillation loss (derivations in tests/test_gpu_distill.py)
+DISTILL_TOL_LOSS = 2e-4
+DISTILL_TOL_DX = 4e-3
+DISTILL_TOL_DW = 3e-3
+DISTILL_TOL_DB = 1e-4
 
 _BITS_VIEW = {"bf16": torch.int16, "fp16": torch.int16, "fp32": torch.int32}
 _NP_BITS = {"bf16": np.uint16, "fp16": np.uint16, "fp32": np.uint32}
@@ -237,8 +244,35 @@ def check(wl: workloads.Workload) -> list[str]:
     return compare_all_rows(wl, g, t)
 
 
+def distill_check(wl: workloads.DistillWorkload) -> list[str]:
+    """The fused linear JSD loss and its gradients on the GPU against the fp64 oracle."""
+    import oracle.distill as od
+    from normalization_row_wise_amd import distill
+    t = workloads.generate_distill(wl)
+    d = {k: (v.to(dev()) if v is not None else None) for k, v in t.items()}
+    loss, dx, dw, db = distill.fused_linear_jsd(d["xs"], d["ws"], d["xt"], d["wt"], d["bs"],
+                                                d["bt"], wl.beta, wl.temperature, wl.chunk)
+    torch.cuda.synchronize()
+    f = lambda a: None if a is None else a.double().numpy()  # noqa: E731
+    o = od.fused_linear_jsd(f(t["xs"]), f(t["ws"]), f(t["bs"]), f(t["xt"]), f(t["wt"]),
+                            f(t["bt"]), wl.beta, wl.temperature)
+    fails = []
+    got = float(loss[0].cpu())
+    if not abs(got - o["loss"]) <= DISTILL_TOL_LOSS * abs(o["loss"]):
+        fails.append(f"{wl.name} loss: {got} vs {o['loss']}")
+    for k, v, tol in (("dx", dx, DISTILL_TOL_DX), ("dw", dw, DISTILL_TOL_DW),
+                      ("db", db, DISTILL_TOL_DB)):
+        if v is None:
+            continue
+        e = rel_l2(v.cpu().double().numpy(), o[k])
+        if not e <= tol:
+            fails.append(f"{wl.name} {k}: rel_l2 {e:.3e}")
+    return fails
+
+
 def smoke_check() -> None:
-    """One small forward + backward of every operation on cuda:0 against the oracle."""
+    """One small forward + backward of every operation, and one small fused linear JSD
+    loss with its gradients, on cuda:0 against the oracle."""
     assert torch.cuda.is_available(), "smoke needs a GPU"
     cases = [
         workloads.small("rmsnorm", 8, 4096, "bf16", eps=1e-6, offset=1.0, weight="gemma", seed=42),
@@ -249,5 +283,8 @@ def smoke_check() -> None:
     fails = []
     for wl in cases:
         fails += check(wl)
+    dl = workloads.DistillWorkload("d96_h64_v1000_bias", 96, 64, 64, 1000, 32, bias=True,
+                                   seed=3)
+    fails += distill_check(dl)
     assert not fails, "\n".join(fails)
-    print("smoke ok:", ", ".join(c.name for c in cases), flush=True)
+    print("smoke ok:", ", ".join([c.name for c in cases] + [dl.name]), flush=True)

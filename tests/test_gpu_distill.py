@@ -21,10 +21,10 @@ from tests import gpu_parity as gp
 
 pytestmark = pytest.mark.gpu
 
-TOL_LOSS = 2e-4
-TOL_DX = 4e-3
-TOL_DW = 3e-3
-TOL_DB = 1e-4
+TOL_LOSS = gp.DISTILL_TOL_LOSS    # 2e-4
+TOL_DX = gp.DISTILL_TOL_DX        # 4e-3
+TOL_DW = gp.DISTILL_TOL_DW        # 3e-3
+TOL_DB = gp.DISTILL_TOL_DB        # 1e-4
 
 
 @pytest.fixture(scope="module", autouse=True)
