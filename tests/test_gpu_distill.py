@@ -162,11 +162,11 @@ def test_full_vocabulary_mid_batch():
     assert gp.rel_l2(dw.double().numpy(), o["dw"]) <= TOL_DW
 
 
-def test_named_size_sampled_tokens():
-    """The page's size (4096 tokens, H = 4096, V = 128256, chunks of 1024): dx of 16
-    sampled tokens against the oracle (each needs only its own logits row), and dx and
-    the loss bit-identical for a frozen head."""
-    wl = workloads.DISTILL_4096x4096_V128256
+@pytest.mark.parametrize("wl", workloads.DISTILL_CONFIGS, ids=lambda c: c.name)
+def test_named_size_sampled_tokens(wl):
+    """The page's sizes (4096 tokens, H = 4096, V = 128256 and 151936, chunks of 1024):
+    dx of 16 sampled tokens against the oracle (each needs only its own logits row), and
+    dx and the loss bit-identical for a frozen head."""
     _say(wl.name)
     t = workloads.generate_distill(wl)
     loss, dx, dw, _ = _run(wl, t)
