@@ -174,6 +174,16 @@ def test_named_size_sampled_tokens(wl):
     assert dwf is None and torch.equal(loss, lf)
     assert torch.equal(dx.view(torch.int16), dxf.view(torch.int16))
     assert bool(torch.isfinite(dw).all()) and bool(torch.isfinite(loss).all())
+    # adding a constant to a token's student logits leaves the loss unchanged, so each
+    # token's logit gradient sums to zero over the vocabulary, and so do the columns of
+    # dW (sum over v of dW[v, :] = sum over t of (sum over v of dz[t, v]) xs[t, :]), up to
+    # the bf16 rounding of dz (relative 2^-9 per element, summing like a random walk:
+    # about 2^-9 / sqrt(V), 5e-6 here, against the column absolute sums)
+    col = dw.double().sum(0)
+    scale = dw.double().abs().sum(0)
+    ratio = float(col.norm() / scale.norm())
+    _say(f"dW column sums / column absolute sums: {ratio:.2e}")
+    assert ratio <= 1e-4
     rows = np.sort(np.random.default_rng(7).choice(wl.BT, 16, replace=False))
     xs, ws = _f64(t["xs"]), _f64(t["ws"])
     zs = xs[rows] @ ws.T
