@@ -51,19 +51,21 @@ extern "C" {
 #endif
 
 /* Workspace bytes of fused_linear_jsd for these sizes and requested gradients
- * (want_* = 0 / 1): two fp32 logit blocks of chunk x V, per-token statistics, and for
- * dx the bf16 logit gradient of a chunk, the transposed student weight and split partial
- * sums; for dw the bf16 transposed logit gradient of all tokens (V x BT) and the
- * transposed student input (H x BT); for db column sums per 64 tokens of a chunk.  A
- * frozen head (want_dw = 0) needs none of the dW buffers ([distill], Summary).  0 for
- * invalid sizes (with want_dw, BT rounded up to 8 must not exceed 2^22). */
+ * (want_* = 0 / 1): two fp32 logit blocks of chunk x V, per-token statistics, the bf16
+ * transposed logit gradient (V x chunk for dx alone, V x BT with dw), for dx split
+ * partial sums, for dw the transposed student input (H x BT), for db column sums per 64
+ * tokens of a chunk.  A frozen head (want_dw = 0) needs none of the dW buffers
+ * ([distill], Summary).  0 for invalid sizes (with want_dw, BT rounded up to 8 must not
+ * exceed 2^22). */
 size_t fused_linear_jsd_workspace_bytes(int64_t BT, int64_t H, int64_t Ht, int64_t V,
                                         int64_t chunk, int want_dx, int want_dw, int want_db);
 
 /* Loss and student gradients.  loss: fp32 [1] out.  dxs: bf16 [BT, H] out (ld lddx) or
  * NULL; dws: fp32 [V, H] out or NULL (frozen weight: no dW product, no dW buffers);
  * dbs: fp32 [V] out or NULL (needs b_s).  All three NULL: forward only.  beta in [0, 1],
- * temperature > 0, 1 <= chunk (tokens per chunk; the products are sized by it).
+ * temperature > 0, 1 <= chunk (tokens per chunk; the products are sized by it; taken
+ * as min(chunk, BT, 2^22) rounded up to a multiple of 8, which changes no result but the
+ * summation order of dbs).
  * ws / ws_bytes: workspace of at least fused_linear_jsd_workspace_bytes(...) bytes,
  * 256-byte aligned, any contents. */
 int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const void* bs,

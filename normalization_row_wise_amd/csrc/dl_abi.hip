@@ -2,12 +2,13 @@
 // argument checks, workspace layout and the chunk loop ([distill], Summary and Details:
 // tokens in chunks, the student head's weight gradient skipped when frozen).
 //
-// Per call: W_s^T once (dx), x_s^T once (dW); per chunk of C tokens: the two logits
-// products (one launch), the per-token statistics, the logit gradient (bf16 rows for dx, bf16 columns
-// of dz^T for dW, fp32 column sums for db), the dx product; after the last chunk one dW
-// product over all tokens.  The fp32 logits (2 C V) are the chunked memory; dz^T is kept
-// for every token (2 bytes per token and vocabulary entry) so that dW is one product with
-// K = tokens instead of an fp32 read-modify-write of [V, H] per chunk.
+// Per call: x_s^T once (dW); per chunk of C tokens: the two logits products (one launch),
+// the per-token statistics, the logit gradient (bf16 columns of dz^T, fp32 column sums
+// for db), the dx product (K-major operands: the chunk's columns of dz^T and W_s as
+// stored); after the last chunk one dW product over all tokens.  The fp32 logits (2 C V)
+// are the chunked memory; with dW, dz^T is kept for every token (2 bytes per token and
+// vocabulary entry) so that dW is one product with K = tokens instead of an fp32
+// read-modify-write of [V, H] per chunk; without it, for the chunk only.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -36,20 +37,28 @@ inline int dx_splits(int64_t chunk, int64_t H) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(8, 256 / std::max<int64_t>(1, tiles))));
 }
 
+// Tokens per chunk: the caller's chunk (at most the batch and 2^22) rounded up to a
+// multiple of 8, so that every chunk's first column of dz^T starts a 16-byte boundary
+// (the dx product reads it as a K-major operand, 64 rows of it at a time with 32-bit
+// offsets).  Chunking changes no value except the fixed summation order of db.
+inline int64_t chunk_rows(int64_t chunk, int64_t BT) {
+  return rup(std::min({chunk, std::max<int64_t>(BT, 1), int64_t(1) << 22}), 8);
+}
+
 // Byte offsets of the workspace parts (each 256-byte aligned); total in `end`.
 struct Layout {
-  size_t zs, zt, stats, gb, wst, dxp, gbt, xst, dbp, jt, end;
-  int64_t C, ldz, vpad, ldt;
+  size_t zs, zt, stats, dxp, gbt, xst, dbp, jt, end;
+  int64_t C, ldz, vpad, ldt;  // ldt: row stride of dz^T (all tokens with dW, else a chunk)
   int splits;
 };
 
 Layout layout(int64_t BT, int64_t H, int64_t V, int64_t chunk, bool dx, bool dw, bool db) {
   Layout L{};
-  const int64_t c = std::min(chunk, std::max<int64_t>(BT, 1));
+  const int64_t c = chunk_rows(chunk, BT);
   L.C = c;
   L.ldz = rup(V, 4);
   L.vpad = rup(V, 8);
-  L.ldt = rup(std::max<int64_t>(BT, 1), 8);
+  L.ldt = dw ? rup(std::max<int64_t>(BT, 1), 8) : c;
   L.splits = dx ? dx_splits(c, H) : 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -60,10 +69,8 @@ Layout layout(int64_t BT, int64_t H, int64_t V, int64_t chunk, bool dx, bool dw,
   L.zs = take(static_cast<size_t>(c) * L.ldz * 4);
   L.zt = take(static_cast<size_t>(c) * L.ldz * 4);
   L.stats = take(static_cast<size_t>(c) * 16);
-  L.gb = dx ? take(static_cast<size_t>(c) * L.vpad * 2) : 0;
-  L.wst = dx ? take(static_cast<size_t>(H) * L.vpad * 2) : 0;
   L.dxp = dx ? take(static_cast<size_t>(L.splits) * c * H * 4) : 0;
-  L.gbt = dw ? take(static_cast<size_t>(V) * L.ldt * 2) : 0;
+  L.gbt = (dx || dw) ? take(static_cast<size_t>(V) * L.ldt * 2) : 0;
   L.xst = dw ? take(static_cast<size_t>(H) * L.ldt * 2) : 0;
   L.dbp = db ? take(static_cast<size_t>(cdiv(c, GR_ROWS)) * V * 4) : 0;
   L.jt = take(static_cast<size_t>(std::max<int64_t>(BT, 1)) * 8);
@@ -81,7 +88,9 @@ bool valid_sizes(int64_t BT, int64_t H, int64_t Ht, int64_t V, int64_t chunk, bo
   if (dw && rup(BT, 8) > (int64_t(1) << 22)) return false;
   // every buffer addressed with 32-bit byte offsets: the weights, a chunk's logits
   if (V * std::max(H, Ht) * 2 >= (int64_t(1) << 32)) return false;
-  if (std::min(chunk, std::max<int64_t>(BT, 1)) * rup(V, 4) * 4 >= (int64_t(1) << 32)) return false;
+  if (chunk_rows(chunk, BT) * rup(V, 4) * 4 >= (int64_t(1) << 32)) return false;
+  // dz^T for a chunk (the dx product's K-major A operand)
+  if (V * chunk_rows(chunk, BT) * 2 >= (int64_t(1) << 32)) return false;
   if (V * H * 4 >= (int64_t(1) << 32)) return false;  // dW
   return true;
 }
@@ -96,7 +105,8 @@ int launch(K k, dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args
              : RN_ERR_HIP;
 }
 
-// The GEMM's two LDS stages exceed the default dynamic LDS limit; raised once per device.
+// The GEMM's two LDS stages exceed the default dynamic LDS limit; raised once per device
+// for both kernels.
 bool allow_gemm_lds() {
   static std::mutex mu;
   static std::set<int> done;
@@ -104,10 +114,12 @@ bool allow_gemm_lds() {
   if (hipGetDevice(&dev) != hipSuccess) return false;
   std::lock_guard<std::mutex> g(mu);
   if (done.count(dev)) return true;
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_nt_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(kGemmLds)) != hipSuccess)
-    return false;
+  for (const void* k : {reinterpret_cast<const void*>(gemm_nt_kernel),
+                        reinterpret_cast<const void*>(gemm_kk_kernel)}) {
+    if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kGemmLds)) != hipSuccess)
+      return false;
+  }
   done.insert(dev);
   return true;
 }
@@ -146,6 +158,19 @@ int gemm(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* 
   gl.grid0 = static_cast<int>(wgs);
   const dim3 grid(static_cast<unsigned>(wgs), 1, static_cast<unsigned>(splits));
   return launch(gemm_nt_kernel, grid, dim3(GT), kGemmLds, s, gl);
+}
+
+// One product with K-major operands: A stored [K][M] (stride lda), B stored [K][N]
+// (stride ldb); bases and strides 16-byte aligned.
+int gemm_kk(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+            int64_t ldc, int64_t split_stride, int64_t M, int64_t N, int64_t K, int splits,
+            hipStream_t s) {
+  if (M == 0 || N == 0) return RN_OK;
+  if (!allow_gemm_lds()) return RN_ERR_HIP;
+  int64_t wgs = 0;
+  const GemmArgs g = gemm_args(A, lda, B, ldb, C, ldc, split_stride, nullptr, M, N, K, splits, wgs);
+  const dim3 grid(static_cast<unsigned>(wgs), 1, static_cast<unsigned>(splits));
+  return launch(gemm_kk_kernel, grid, dim3(GT), kGemmLds, s, g);
 }
 
 // Two products of the same M x N (no split) in one launch: C0 = A0 B0^T (+ bias0) with
@@ -209,10 +234,8 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
   float* zs = reinterpret_cast<float*>(base + L.zs);
   float* zt = reinterpret_cast<float*>(base + L.zt);
   float* stats = reinterpret_cast<float*>(base + L.stats);
-  uint16_t* gb = want_dx ? reinterpret_cast<uint16_t*>(base + L.gb) : nullptr;
-  uint16_t* wst = want_dx ? reinterpret_cast<uint16_t*>(base + L.wst) : nullptr;
   float* dxp = want_dx ? reinterpret_cast<float*>(base + L.dxp) : nullptr;
-  uint16_t* gbt = want_dw ? reinterpret_cast<uint16_t*>(base + L.gbt) : nullptr;
+  uint16_t* gbt = (want_dx || want_dw) ? reinterpret_cast<uint16_t*>(base + L.gbt) : nullptr;
   uint16_t* xst = want_dw ? reinterpret_cast<uint16_t*>(base + L.xst) : nullptr;
   float* dbp = want_db ? reinterpret_cast<float*>(base + L.dbp) : nullptr;
   double* jt = reinterpret_cast<double*>(base + L.jt);
@@ -238,8 +261,6 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
     return RN_OK;
   }
 
-  // W_s^T [H][vpad] (zero columns past V): the K-contiguous operand of the dx product
-  if (want_dx && (e = transpose(Ws, H, V, H, wst, L.vpad, L.vpad, st)) != RN_OK) return e;
   // x_s^T [H][ldt] (zero columns past BT): the second operand of the dW product
   if (want_dw && (e = transpose(Xs, ldxs, BT, H, xst, L.ldt, L.ldt, st)) != RN_OK) return e;
 
@@ -263,27 +284,29 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
     if ((e = launch(jsd_stats_kernel, dim3(static_cast<unsigned>(cr)), dim3(JT), 0, st, sa)) != RN_OK)
       return e;
     if (!want_grad) continue;
-    // dL/dz: bf16 rows (dx), bf16 columns of dz^T (dW; the last chunk also zeroes the
-    // token padding), fp32 column sums per 64 rows (db)
+    // dL/dz: bf16 columns of dz^T (dx and dW: all tokens' columns with dW, the last chunk
+    // also zeroing the token padding; the chunk's alone without), fp32 column sums per
+    // 64 rows (db)
+    const int64_t tok0 = want_dw ? c0 : 0;  // the chunk's first column of dz^T
     GradArgs ga{};
     ga.zs = zs; ga.zt = zt; ga.ldz = L.ldz; ga.stats = stats;
     ga.rows = static_cast<int>(cr); ga.V = static_cast<int>(V);
     ga.beta = beta; ga.inv_tau = inv_tau;
     ga.grad_scale = static_cast<float>(1.0 / (static_cast<double>(temperature) * static_cast<double>(BT)));
-    ga.gb = gb; ga.ldg = L.vpad; ga.vpad = static_cast<int>(L.vpad);
-    ga.gbt = gbt; ga.ldt = L.ldt; ga.tok0 = c0;
-    ga.tok_rows = static_cast<int>(last ? L.ldt - c0 : cr);
+    ga.gb = nullptr; ga.ldg = 0; ga.vpad = static_cast<int>(L.vpad);
+    ga.gbt = gbt; ga.ldt = L.ldt; ga.tok0 = tok0;
+    ga.tok_rows = static_cast<int>(want_dw && last ? L.ldt - c0 : cr);
     ga.dbp = dbp;
-    const int64_t grid_rows = want_dw ? std::max<int64_t>(cr, ga.tok_rows) : cr;
+    const int64_t grid_rows = std::max<int64_t>(cr, ga.tok_rows);
     if ((e = launch(jsd_grad_kernel,
                     dim3(static_cast<unsigned>(cdiv(L.vpad, GR_COLS)),
                          static_cast<unsigned>(cdiv(grid_rows, GR_ROWS))),
                     dim3(GR_T), 0, st, ga)) != RN_OK)
       return e;
     if (want_dx) {
-      // dx[c0 .. c0 + cr) = dz W_s: K = V in `splits` ranges, then their fixed-order sum
-      if ((e = gemm(gb, L.vpad, wst, L.vpad, dxp, H, cr * H, nullptr, cr, H, L.vpad, L.splits,
-                    st)) != RN_OK)
+      // dx[c0 .. c0 + cr) = dz W_s with K-major operands (dz^T's chunk columns, W_s as
+      // stored): K = V in `splits` ranges, then their fixed-order sum
+      if ((e = gemm_kk(gbt + tok0, L.ldt, Ws, H, dxp, H, cr * H, cr, H, V, L.splits, st)) != RN_OK)
         return e;
       if ((e = launch(split_sum_bf16_kernel, dim3(static_cast<unsigned>(cdiv(cr * H, 256))),
                       dim3(256), 0, st, static_cast<const float*>(dxp), cr * H, L.splits,
