@@ -293,7 +293,6 @@ int fused_linear_jsd(const void* xs, int64_t ldxs, const void* ws_weight, const 
     ga.rows = static_cast<int>(cr); ga.V = static_cast<int>(V);
     ga.beta = beta; ga.inv_tau = inv_tau;
     ga.grad_scale = static_cast<float>(1.0 / (static_cast<double>(temperature) * static_cast<double>(BT)));
-    ga.gb = nullptr; ga.ldg = 0; ga.vpad = static_cast<int>(L.vpad);
     ga.gbt = gbt; ga.ldt = L.ldt; ga.tok0 = tok0;
     ga.tok_rows = static_cast<int>(want_dw && last ? L.ldt - c0 : cr);
     ga.dbp = dbp;

@@ -179,16 +179,15 @@ struct GradArgs {
   int rows, V;                                    // token rows of the chunk
   float beta, inv_tau;
   float grad_scale;                               // 1 / (tau * tokens)
-  uint16_t* gb; int64_t ldg; int vpad;            // bf16 dz [rows][ldg], zeros in [V, vpad); or null
   uint16_t* gbt; int64_t ldt; int64_t tok0;       // bf16 dz^T: gbt[v][tok0 + r]; or null
   int tok_rows;                                   // rows r < tok_rows written to gbt (zeros past rows)
   float* dbp;                                     // [row tiles][V] column sums, or null
 };
 
-// dz for a tile, written as bf16 rows (the dx product's A operand), as bf16 columns of
-// dz^T through LDS (the dW product's A operand: 128 contiguous bytes per vocabulary row),
-// and as fp32 column sums of the tile's rows (db, fixed order).  The value of dz does not
-// depend on which of the three are written.
+// dz for a tile, written as bf16 columns of dz^T through LDS (the A operand of the dx
+// and dW products: 128 contiguous bytes per vocabulary row) and as fp32 column sums of
+// the tile's rows (db, fixed order).  The value of dz does not depend on which are
+// written.
 __global__ __launch_bounds__(GR_T) void jsd_grad_kernel(GradArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[GR_ROWS * GR_PITCH];
   __shared__ float colsum[4][GR_COLS];
@@ -224,12 +223,6 @@ __global__ __launch_bounds__(GR_T) void jsd_grad_kernel(GradArgs a) {
           dz[k] = a.grad_scale * s * (g - st.z);
           cs[k] += dz[k];
         }
-      }
-      if (a.gb != nullptr && v < a.vpad) {
-        uint2 p;
-        p.x = static_cast<uint32_t>(f_to_bf16(dz[0])) | (static_cast<uint32_t>(f_to_bf16(dz[1])) << 16);
-        p.y = static_cast<uint32_t>(f_to_bf16(dz[2])) | (static_cast<uint32_t>(f_to_bf16(dz[3])) << 16);
-        *reinterpret_cast<uint2*>(a.gb + static_cast<int64_t>(row) * a.ldg + v) = p;
       }
     }
     if (a.gbt != nullptr) {
