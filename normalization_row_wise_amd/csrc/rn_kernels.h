@@ -406,8 +406,8 @@ template <int V, int ACC, int S> struct Acc {
 };
 
 // Register accumulators (ACC = 0): the R teams' sums are added in team order through
-// `part` and team 0 writes the workgroup's partial row `dst` (columns past N are not
-// written).
+// `part` and team 0 writes the workgroup's partial row `dst` (16-byte aligned; columns
+// past N are not written).
 template <int V, bool VEC, int EVE, int DX, int S>
 __device__ __forceinline__ void combine_regs(const Acc<V, 0, S>& acc, float* dst, float* part, int r,
                                              int R, int t, int T, int N) {
@@ -429,10 +429,24 @@ __device__ __forceinline__ void combine_regs(const Acc<V, 0, S>& acc, float* dst
     }
   }
   if (r == 0) {
+    if constexpr (VEC) {
+      static_assert(FX::VE % 4 == 0, "16-byte accesses hold 4 or 8 elements");
+      // elements 4 j .. 4 j + 3 are four adjacent columns of one access (VE = 4 or 8),
+      // wholly inside or outside the row (N is a multiple of VE): one 16-byte store
+      // each instead of four 4-byte stores whose lanes lie 32 bytes apart
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int c = FX::col(i, t, T);
-      if (c < N) dst[c] = tot[i];
+      for (int j = 0; j < V / 4; ++j) {
+        const int c0 = FX::col(4 * j, t, T);
+        if (c0 < N)
+          *reinterpret_cast<float4*>(dst + c0) =
+              make_float4(tot[4 * j], tot[4 * j + 1], tot[4 * j + 2], tot[4 * j + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int c = FX::col(i, t, T);
+        if (c < N) dst[c] = tot[i];
+      }
     }
   }
 }
